@@ -1,0 +1,182 @@
+/*
+ * pc.h -- C ABI of the MI355X collective datapath library (libpcdp.so).
+ *
+ * The library implements one GPU's share of the all-reduce / all-gather
+ * datapath: an N-way elementwise reduction of N rank-staged bf16 buffers in a
+ * fixed rank order, sequence-number ("LL") line packing and consume-side
+ * readiness validation, the twoshot split (slice reduce, then copy-out), and
+ * an all-gather copy whose blocks carry sequence-number headers.  The N
+ * peers' staged buffers are N distinct device regions.
+ *
+ * Conventions shared by every call:
+ *  - All functions are extern "C", return pc_status and never throw.
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *  - Pointer arrays (`inputs`, `lines`, `outs`, `shards`) and `order` are HOST
+ *    arrays, read only during the call.  The pointers inside them and every
+ *    other data pointer are DEVICE pointers on the current HIP device, each
+ *    16-byte aligned.  The caller allocates and frees all memory; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; outputs are valid once the stream has
+ *    reached the call.  No call synchronizes the device.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is launched and outputs are untouched.  A size of zero is a
+ *    legal no-op (PC_OK); its device pointers are then not examined.
+ *  - Calls that overlap in time on the same output buffers race; calls on
+ *    different streams touching disjoint buffers are independent.
+ *
+ * Arithmetic (every reduction here):
+ *  Each output element is y = narrow(((-0.0f + w(x_{o0})) + w(x_{o1})) + ... +
+ *  w(x_{o(n-1)})) where w() widens bf16 to fp32 exactly, each addition is an
+ *  IEEE binary32 addition rounded to nearest-even with subnormals kept, and
+ *  narrow() rounds fp32 to bf16 to nearest-even, overflow giving +-Inf and any
+ *  NaN giving the canonical quiet NaN 0x7FC0.  o0..o(n-1) is ascending rank
+ *  order unless `order` says otherwise.  The result is bit-exact: one correct
+ *  bit pattern per element.
+ *  ("Purlin: Separating Orchestration from the Datapath of Collectives",
+ *  Section 3.3, Equation (2); "flash-comm: Self-Synchronizing Collective
+ *  Communication for LLM Decoding", Section 3.3.)
+ */
+#ifndef PC_H
+#define PC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int pc_status;
+
+enum {
+    PC_OK = 0,
+    PC_EINVAL = -1,       /* bad argument: n out of range, NULL pointer,     */
+                          /* order not a permutation, seq == 0, overlapping  */
+                          /* buffers, size above the maximum                 */
+    PC_EALIGN = -2,       /* a device pointer or a size is misaligned        */
+    PC_EUNSUPPORTED = -3, /* reserved                                        */
+    PC_EHIP = -4          /* the HIP runtime refused the launch              */
+};
+
+#define PC_ABI_VERSION 1
+#define PC_MAX_RANKS 8
+#define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
+#define PC_BLOCK_PAYLOAD_BYTES 128
+#define PC_BLOCK_RECORD_BYTES 136   /* u64 seq header, then 128 payload bytes           */
+#define PC_MAX_ELEMS ((size_t)1 << 34) /* largest k accepted per rank (32 GiB of bf16) */
+
+/*
+ * pc_reduce -- N-way rank-ordered reduction (oneshot's local reduce).
+ * Source: Purlin, Section 3.3 (Listing 3's reduce over n equally sized typed
+ * sources into one destination; Equation (2) for the arithmetic); SiFAR:
+ * Synchronization-Free All-Reduce for Low-Latency LLM Inference, Section 3.1
+ * (oneshot: every GPU reduces all N buffers elementwise).
+ *   inputs : host array of n device pointers, each to k bf16 values.  Inputs
+ *            may alias each other.
+ *   n      : 1..PC_MAX_RANKS.
+ *   out    : device pointer to k bf16 values.  It may be exactly one of the
+ *            inputs (in place); any other overlap with an input is PC_EINVAL.
+ *   k      : elements per rank; multiple of 8, at most PC_MAX_ELEMS.
+ *   order  : host array, a permutation of 0..n-1 giving the fold order, or
+ *            NULL for 0,1,..,n-1.
+ * Errors: PC_EINVAL, PC_EALIGN (pointer not 16-byte aligned, k % 8 != 0),
+ *         PC_EHIP.
+ */
+pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t k,
+                    const int32_t* order, void* stream);
+
+/*
+ * pc_pack_ll -- stage k bf16 values as k/2 sequence-stamped 8-byte lines.
+ * Source: flash-comm, Section 3.1 (sequence-number readiness: data and the
+ * call's sequence number share one transfer unit) and Section 4.3 (16-byte
+ * packets of 8 payload bytes and two copies of the sequence number, i.e. two
+ * such lines); Purlin, Section 3.2 (latency path: payload packed with a flag).
+ *   src  : device, k bf16 values.
+ *   dst  : device, k/2 uint64 lines; line j = (src[2j] | src[2j+1] << 16)
+ *          | (uint64)seq << 32 (little-endian: data bytes 0..3, seq 4..7).
+ *          Must not overlap src.
+ *   k    : multiple of 8, at most PC_MAX_ELEMS.
+ *   seq  : the current call's sequence number, nonzero (zero-filled memory
+ *          must never read as ready).
+ * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
+ */
+pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32_t seq, void* stream);
+
+/*
+ * pc_consume_ll -- validate N ranks' LL lines and fold the ready ones.
+ * Source: flash-comm, Section 4.3 (one-hop: poll the source slots, reduce only
+ * once all contributions are available, fold by source rank in rank order),
+ * Section 3.1 (accept a unit only when its sequence number matches the
+ * current call), Section 3.3 (rank order 0..N-1).
+ *   lines  : host array of n device pointers, each to k/2 uint64 lines.
+ *   out    : device, k bf16.  For every line j that is ready on all n ranks,
+ *            out[2j], out[2j+1] = the rank-ordered fold of the lines' two
+ *            halves.  Output of a line that is not ready is left untouched.
+ *   k      : multiple of 128 (whole bitmap words), at most PC_MAX_ELEMS.
+ *   seq    : nonzero; a line is current iff its high 32 bits equal seq.
+ *   ready_bitmap : device, k/128 uint64 words; bit (j & 63) of word (j >> 6)
+ *            is 1 iff line j was ready.  Every word is written.
+ *   out, ready_bitmap and the lines must not overlap one another.
+ * Errors: PC_EINVAL, PC_EALIGN (pointer alignment, k % 128 != 0), PC_EHIP.
+ */
+pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* out, size_t k,
+                        uint32_t seq, uint64_t* ready_bitmap, void* stream);
+
+/*
+ * pc_twoshot -- reduce-scatter by slice owner, then copy-out to every rank.
+ * Source: SiFAR, Section 3.1 and Figure 6 (twoshot: each GPU reduces one
+ * portion, then broadcasts it to all peers); flash-comm, Section 3.3 (each
+ * output block has one owner that reduces it once and distributes it) and
+ * Section 4.3 (sharded two-hop); Purlin, Section 3.1 (AllReduce as a
+ * ReduceScatter followed by an AllGather, Figure 4).
+ *   inputs : host array of n device pointers, k bf16 each.
+ *   outs   : host array of n device pointers, k bf16 each, pairwise
+ *            disjoint.  Slice s = [s*k/n, (s+1)*k/n) is folded in rank order
+ *            0..n-1 into outs[s] (its owner), then copied from outs[s] into
+ *            every other outs[r].  Every outs[r] equals pc_reduce's result
+ *            bit for bit.  outs[r] may be exactly an input buffer (in place);
+ *            other overlaps with inputs are PC_EINVAL.
+ *   k      : multiple of 8*n, at most PC_MAX_ELEMS.
+ * Two kernels are enqueued on `stream`, the copy-out after the slice reduce.
+ * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
+ */
+pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
+                     void* stream);
+
+/*
+ * pc_allgather_copy -- gather N shards of sequence-stamped blocks.
+ * Source: flash-comm, Section 4.3 (all-gather: every source publishes one
+ * shard, receivers wait on the same readiness layer and place each shard in
+ * the output) and Appendix A, Table 8 discussion (128-byte writes arrive
+ * whole); Purlin, Section 3.1 (AllGather output is rank-ordered).
+ *   shards : host array of n device pointers.  Shard r holds B =
+ *            shard_bytes/128 records of 136 bytes: a uint64 sequence header,
+ *            then 128 payload bytes.
+ *   out    : device, n*shard_bytes bytes (n*shard_bytes/2 bf16).  Record b
+ *            of shard r whose header equals seq is copied to bytes
+ *            [(r*B + b)*128, +128); a record that does not match leaves those
+ *            bytes untouched.
+ *   shard_bytes : payload bytes per shard; multiple of 8192 (64 blocks, one
+ *            bitmap word), at most 2*PC_MAX_ELEMS.
+ *   seq    : nonzero; compared with the whole 64-bit header.
+ *   ready_bitmap : device, n*B/64 uint64 words; bit i (LSB-first) is 1 iff
+ *            block i = r*B + b was copied.  Every word is written.
+ *   out, ready_bitmap and the shards must not overlap one another.
+ * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
+ */
+pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
+                            size_t shard_bytes, uint64_t seq, uint64_t* ready_bitmap,
+                            void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* pc_strerror(pc_status status);
+
+/* PC_ABI_VERSION of the loaded library. */
+int pc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PC_H */

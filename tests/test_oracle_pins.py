@@ -1,0 +1,340 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+  * hand-derived closed forms from tests/golden/closed_forms.json;
+  * library routines: torch's CPU bfloat16 conversions (finite values) and
+    numpy float32 elementwise addition taken one rank at a time;
+  * brute force over every bf16 pattern, and over tiny inputs;
+  * invariants the pages fix (one owner per slice equals the oneshot fold,
+    pack-then-consume is the identity, stale sequence numbers are rejected).
+Each group is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong sign, a wrong index, swapped operands, an off-by-one rounding bit)
+fails at least one test.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from collective_datapath_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+CANON_NAN = 0x7FC0
+
+
+def h(s):
+    return int(s, 16)
+
+
+# --- library references (torch conversions, numpy float32 adds) ----------
+
+def lib_widen(u16):
+    t = torch.from_numpy(np.ascontiguousarray(u16, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).float().numpy()
+
+
+def lib_narrow(f32):
+    f32 = np.ascontiguousarray(f32, dtype=np.float32)
+    out = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    out[np.isnan(f32)] = CANON_NAN
+    return out
+
+
+def lib_reduce(xs, order=None):
+    order = range(len(xs)) if order is None else order
+    acc = np.full(xs[0].size, -0.0, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for r in order:
+            acc = acc + lib_widen(xs[r])
+    return lib_narrow(acc)
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# --- conversions ---------------------------------------------------------
+
+def test_narrow_closed_forms(orc, golden):
+    for case in golden["narrow"]["cases"]:
+        f = np.array([h(case["f32"])], dtype=np.uint32).view(np.float32)
+        got = int(orc.narrow(f)[0])
+        assert got == h(case["bf16"]), (case, hex(got))
+
+
+def test_narrow_matches_library_on_rounding_boundaries(orc):
+    # Every bf16 upper half combined with the low halves that decide rounding.
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x3FFF, 0x4000, 0x7FFE, 0x7FFF, 0x8000, 0x8001,
+                     0x8002, 0xBFFF, 0xC000, 0xFFFE, 0xFFFF], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).reshape(-1)
+    f = u.view(np.float32)
+    assert np.array_equal(orc.narrow(f), lib_narrow(f))
+
+
+def test_narrow_matches_library_random(orc):
+    g = np.random.default_rng(11)
+    u = g.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    f = u.view(np.float32)
+    assert np.array_equal(orc.narrow(f), lib_narrow(f))
+
+
+def test_nan_becomes_canonical(orc):
+    g = np.random.default_rng(12)
+    mant = g.integers(1, 1 << 23, size=1 << 16, dtype=np.uint32)
+    sign = g.integers(0, 2, size=mant.size, dtype=np.uint32) << 31
+    u = sign | np.uint32(0x7F800000) | mant
+    assert np.all(orc.narrow(u.view(np.float32)) == CANON_NAN)
+
+
+def test_widen_matches_library_exhaustive(orc):
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    a = orc.widen(allh).view(np.uint32)
+    b = lib_widen(allh).view(np.uint32)
+    assert np.array_equal(a, b)
+
+
+def test_widen_then_narrow_is_identity_except_nan(orc):
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    back = orc.narrow(orc.widen(allh))
+    isnan = ((allh & 0x7FFF) > 0x7F80)
+    assert np.array_equal(back[~isnan], allh[~isnan])
+    assert np.all(back[isnan] == CANON_NAN)
+
+
+# --- the fold ------------------------------------------------------------
+
+def test_fold_closed_forms(orc, golden):
+    for case in golden["fold"]["cases"]:
+        xs = [np.full(24, h(v), dtype=np.uint16) for v in case["inputs"]]
+        out = orc.reduce(xs, order=case["order"])
+        assert np.all(out == h(case["bf16"])), (case, hex(int(out[0])))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+def test_fold_constant_ranks_sum_exactly(orc, n):
+    # Rank r filled with c_r = (r+1)/8: every partial sum is exact in fp32,
+    # so the result is the bf16 of sum(c_r) = n(n+1)/16 whatever went before.
+    xs = [lib_narrow(np.full(4096, (r + 1) / 8, dtype=np.float32)) for r in range(n)]
+    want = lib_narrow(np.array([n * (n + 1) / 16], dtype=np.float32))[0]
+    assert np.all(orc.reduce(xs) == want)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 8])
+def test_fold_matches_library_sequential_adds(orc, n):
+    xs = [synth.uniform_bf16(90, 0, r, 40_000) for r in range(n)]
+    assert np.array_equal(orc.reduce(xs), lib_reduce(xs))
+
+
+def test_fold_order_is_honoured(orc):
+    # Mixed magnitudes make the fold order visible in the rounded result.
+    g = np.random.default_rng(5)
+    xs = [synth.f32_to_bf16_bits_trunc(g.standard_normal(50_000).astype(np.float32)
+                                      * np.float32(10.0 ** (3 * (r % 3))))
+          for r in range(6)]
+    order = [5, 2, 0, 4, 1, 3]
+    a = orc.reduce(xs, order=order)
+    assert np.array_equal(a, lib_reduce(xs, order))
+    assert not np.array_equal(a, orc.reduce(xs)), "test data must be order-sensitive"
+    # A pairwise (tree) sum of the same data differs: the oracle is sequential.
+    w = [lib_widen(x) for x in xs]
+    pair = lib_narrow(((w[0] + w[1]) + (w[2] + w[3])) + (w[4] + w[5]))
+    assert not np.array_equal(orc.reduce(xs), pair)
+
+
+def test_fold_rejects_bad_order(orc):
+    xs = [np.zeros(8, np.uint16)] * 3
+    for bad in ([0, 0, 1], [0, 1, 3], [-1, 0, 1]):
+        with pytest.raises(ValueError):
+            orc.reduce(xs, order=bad)
+
+
+def test_fold_threads_do_not_change_bits(orc):
+    xs = [synth.normal_bf16(91, 0, r, 100_003) for r in range(8)]
+    a = orc.reduce(xs, threads=1)
+    for t in (2, 5, 8):
+        assert np.array_equal(a, orc.reduce(xs, threads=t))
+
+
+def test_fold_brute_force_two_ranks(orc):
+    # Every bf16 pattern as rank 0 against 48 partners each (specials included).
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F,
+                         0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x3F80, 0xBF80, 0x4C00, 0xCC00],
+                        dtype=np.uint16)
+    g = np.random.default_rng(13)
+    partners = np.concatenate([specials, g.integers(0, 1 << 16, 32).astype(np.uint16)])
+    x0 = np.repeat(allh, partners.size)
+    x1 = np.tile(partners, allh.size)
+    assert np.array_equal(orc.reduce([x0, x1]), lib_reduce([x0, x1]))
+    assert np.array_equal(orc.reduce([x1, x0]), lib_reduce([x1, x0]))
+
+
+def test_fold_brute_force_three_ranks_specials(orc):
+    sp = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80,
+                   0x7FC0, 0x3F80, 0xBF80, 0x4C00, 0xCC00, 0x3B80], dtype=np.uint16)
+    a, b, c = np.meshgrid(sp, sp, sp, indexing="ij")
+    xs = [a.reshape(-1), b.reshape(-1), c.reshape(-1)]
+    for order in ([0, 1, 2], [2, 1, 0], [1, 2, 0]):
+        assert np.array_equal(orc.reduce(xs, order=order), lib_reduce(xs, order))
+
+
+# --- LL lines ------------------------------------------------------------
+
+def test_pack_ll_closed_forms(orc, golden):
+    for case in golden["pack_ll"]["cases"]:
+        src = np.array([h(v) for v in case["src"]], dtype=np.uint16)
+        lines = orc.pack_ll(src, case["seq"])
+        assert [int(v) for v in lines] == [h(v) for v in case["lines"]]
+
+
+def test_pack_ll_layout_by_views(orc):
+    src = synth.uniform_bf16(92, 0, 0, 8192)
+    lines = orc.pack_ll(src, 0x01020304)
+    words = lines.view(np.uint32)               # little-endian: low word first
+    assert np.array_equal(words[0::2], src.view(np.uint32))
+    assert np.all(words[1::2] == 0x01020304)
+
+
+def test_consume_one_rank_is_identity(orc):
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    out, bm = orc.consume_ll([orc.pack_ll(allh, 9)], allh.size, 9)
+    isnan = ((allh & 0x7FFF) > 0x7F80)
+    assert np.array_equal(out[~isnan], allh[~isnan])
+    assert np.all(out[isnan] == CANON_NAN)
+    assert np.all(bm == np.uint64(0xFFFFFFFFFFFFFFFF))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_consume_all_current_equals_reduce(orc, n):
+    xs = [synth.uniform_bf16(93, 0, r, 16384) for r in range(n)]
+    out, bm = orc.consume_ll([orc.pack_ll(x, 7) for x in xs], 16384, 7)
+    assert np.array_equal(out, lib_reduce(xs))
+    assert np.all(bm == np.uint64(0xFFFFFFFFFFFFFFFF))
+
+
+def test_consume_wrong_seq_rejects_everything(orc):
+    xs = [synth.uniform_bf16(94, 0, r, 4096) for r in range(4)]
+    lines = [orc.pack_ll(x, 7) for x in xs]
+    for seq in (6, 8, 7 + (1 << 31)):
+        out, bm = orc.consume_ll(lines, 4096, seq)
+        assert np.all(bm == 0)
+        assert np.all(out == 0xFFFF)
+
+
+def test_consume_one_hot_stale_pins_bit_and_index(orc):
+    n, k = 4, 1024
+    xs = [synth.uniform_bf16(95, 0, r, k) for r in range(n)]
+    lines = [orc.pack_ll(x, 7) for x in xs]
+    j = 70                                      # word 1, bit 6
+    lines[3] = lines[3].copy()
+    lines[3][j] = (lines[3][j] & np.uint64(0xFFFFFFFF)) | (np.uint64(6) << np.uint64(32))
+    out, bm = orc.consume_ll(lines, k, 7)
+    want_bm = np.full(k // 128, 0xFFFFFFFFFFFFFFFF, dtype=np.uint64)
+    want_bm[1] &= ~np.uint64(1 << 6)
+    assert np.array_equal(bm, want_bm)
+    ref = lib_reduce(xs)
+    ref[2 * j:2 * j + 2] = 0xFFFF
+    assert np.array_equal(out, ref)
+
+
+def _stage_ll(orc, case, k=None):
+    """Staged line buffers of an LL workload: stale lines carry the stale seq
+    and the stale payload (what the slot held from the previous call)."""
+    staged = []
+    for x, s, m in zip(case.payloads(), case.stale_payloads(), case.stale_masks()):
+        cur = orc.pack_ll(x, case.seq)
+        old = orc.pack_ll(s, case.stale_seq)
+        staged.append(np.where(m, old, cur))
+    return staged
+
+
+def test_consume_stale_workload_popcount_and_values(orc):
+    case = synth.C2_LL_128K
+    masks = case.stale_masks()
+    assert all(int(m.sum()) == 1638 for m in masks)
+    staged = _stage_ll(orc, case)
+    out, bm = orc.consume_ll(staged, case.k, case.seq)
+    ready = ~np.logical_or.reduce(masks)
+    bits = np.unpackbits(bm.view(np.uint8), bitorder="little").astype(bool)
+    assert np.array_equal(bits, ready)
+    ref = lib_reduce(case.payloads())
+    want = np.where(np.repeat(ready, 2), ref, np.uint16(0xFFFF))
+    assert np.array_equal(out, want)
+    # Accepting stale lines would change the output (the check is sensitive).
+    nostale = lib_reduce([np.where(np.repeat(m, 2), s, x) for x, s, m in
+                          zip(case.payloads(), case.stale_payloads(), masks)])
+    assert np.count_nonzero(nostale != ref) > 0.3 * case.k
+
+
+def test_consume_late_arrival_converges(orc):
+    case = synth.LLCase("small", 96, 8, 8192)
+    staged = _stage_ll(orc, case)
+    out, bm = orc.consume_ll(staged, case.k, case.seq)
+    assert 0 < int(np.unpackbits(bm.view(np.uint8)).sum()) < case.lines
+    # The late lines land with the current seq; a second consume finishes.
+    landed = [orc.pack_ll(x, case.seq) for x in case.payloads()]
+    out2, bm2 = orc.consume_ll(landed, case.k, case.seq, out=out)
+    assert np.all(bm2 == np.uint64(0xFFFFFFFFFFFFFFFF))
+    assert np.array_equal(out2, lib_reduce(case.payloads()))
+
+
+# --- twoshot -------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(8, 8 * 8 * 97), (4, 4 * 8 * 33), (3, 3 * 8 * 5), (1, 64)])
+def test_twoshot_every_output_is_the_oneshot_fold(orc, n, k):
+    xs = [synth.normal_bf16(97, 0, r, k) for r in range(n)]
+    outs = orc.twoshot(xs)
+    ref = lib_reduce(xs)
+    for o in outs:
+        assert np.array_equal(o, ref)
+
+
+def test_twoshot_workload_shape(orc):
+    case = synth.C3_TWOSHOT_1M
+    xs = case.inputs()
+    outs = orc.twoshot(xs)
+    ref = lib_reduce(xs)
+    assert all(np.array_equal(o, ref) for o in outs)
+
+
+# --- all-gather copy -----------------------------------------------------
+
+def test_allgather_all_current_is_concatenation(orc):
+    case = synth.GatherCase("all current", 98, 4, 16384, stale_frac=0.0)
+    recs, _ = case.records()
+    out, bm = orc.allgather_copy(recs, case.shard_bytes, case.seq)
+    assert np.array_equal(out, np.concatenate(case.payloads()))
+    assert np.all(bm == np.uint64(0xFFFFFFFFFFFFFFFF))
+
+
+def test_allgather_one_hot_stale_pins_position(orc):
+    case = synth.GatherCase("one stale", 99, 3, 8192, stale_frac=0.0)
+    recs, _ = case.records()
+    r, b = 2, 37                                 # item 2*64 + 37 = 165: word 2, bit 37
+    recs[r] = recs[r].copy()
+    recs[r].view(np.uint64)[17 * b] = np.uint64(6)
+    out, bm = orc.allgather_copy(recs, case.shard_bytes, case.seq)
+    want_bm = np.full(3, 0xFFFFFFFFFFFFFFFF, dtype=np.uint64)
+    want_bm[2] &= ~np.uint64(1 << 37)
+    assert np.array_equal(bm, want_bm)
+    want = np.concatenate(case.payloads())
+    item = r * 64 + b
+    want[item * 64:(item + 1) * 64] = 0xFFFF
+    assert np.array_equal(out, want)
+
+
+def test_allgather_stale_workload(orc):
+    case = synth.C5_ALLGATHER_2M
+    recs, masks = case.records()
+    out, bm = orc.allgather_copy(recs, case.shard_bytes, case.seq)
+    bits = np.unpackbits(bm.view(np.uint8), bitorder="little").astype(bool)
+    ready = ~np.concatenate(masks)
+    assert np.array_equal(bits, ready)
+    assert int(bits.sum()) == 131072 - 8 * 1638
+    want = np.where(np.repeat(ready, 64), np.concatenate(case.payloads()), np.uint16(0xFFFF))
+    assert np.array_equal(out, want)
