@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X collective datapath (one GPU).
+
+Headline: effective HBM GB/s of the bandwidth-regime oneshot reduce (8 ranks
+x 64 MiB bf16, fp32 accumulation in rank order 0..7, bf16 output) with the
+inputs resident in HBM, as a fraction of the 8 TB/s HBM peak; beside it the
+per-call latency of every datapath call on the decode-shaped workloads and a
+latency sweep from 8 KiB to 1 MiB per rank.  Every timed workload is checked
+bit for bit against the CPU oracle after timing, and the oracle itself is
+timed on the host cores on the headline workload.
+
+Timing:
+  * kernel time per launch: HIP events (torch.cuda.Event, recorded on the
+    stream the library launches on) around `--steps` back-to-back calls;
+  * per-call time in a graph: 128 calls captured in one HIP graph, replayed
+    once to warm up, then 8 replays timed with events, divided by 1024;
+  * empty-kernel floor: the same two measurements of an empty kernel.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed calls of the headline workload")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="all",
+                    choices=["all", "headline", "c1", "c2", "c3", "c5", "sweep", "copy"],
+                    help="run one part only (profiling); 'copy' times a plain device copy")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    return ap.parse_args()
+
+
+class Dev:
+    """Device plumbing: uploads and timing."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.dev = torch.device("cuda:0")
+
+    def up(self, a):
+        a = np.ascontiguousarray(a)
+        v = {np.dtype(np.uint16): np.int16, np.dtype(np.uint64): np.int64,
+             np.dtype(np.uint8): np.uint8}[a.dtype]
+        return self.torch.from_numpy(a.view(v)).to(self.dev)
+
+    def down(self, t, dt):
+        self.torch.cuda.synchronize()
+        return t.cpu().numpy().view(dt)
+
+    def events_ms(self, fn, steps, warmup):
+        """Average ms per call over `steps` back-to-back calls (events)."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def graph_us(self, fn, calls=128, replays=8):
+        """Per-call us: `calls` calls in one graph, 1 warm replay, `replays` timed."""
+        torch = self.torch
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(calls):
+                    fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) * 1000.0 / (calls * replays)
+
+
+def timing(d, fn, steps, warmup):
+    ms = d.events_ms(fn, steps, warmup)
+    return {"kernel_us": round(ms * 1000.0, 3), "graph_us": round(d.graph_us(fn), 3)}
+
+
+def gbs(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
+
+
+# ---------------------------------------------------------------------------
+
+
+def run_headline(d, B, synth, args, out):
+    case = synth.C4_ONESHOT_64M
+    log("generating", case.name)
+    xs = case.inputs()
+    ins = [d.up(x) for x in xs]
+    res = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
+    fn = lambda: B.pc_reduce(ins, res, case.k)  # noqa: E731
+    log("timing headline:", args.steps, "calls after", args.warmup, "warm-up")
+    ms = d.events_ms(fn, args.steps, args.warmup)
+    g_us = d.graph_us(fn, calls=16, replays=4)
+    nbytes = case.bytes_moved()
+    ach = gbs(nbytes, ms * 1000.0)
+    out["headline"] = {"workload": case.name, "bytes_per_call": nbytes, "kernel_us": round(ms * 1e3, 3),
+                       "graph_us": round(g_us, 3), "gbs": round(ach, 1)}
+    got = d.down(res, np.uint16)
+    if not args.no_parity or not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        runs = []
+        want = None
+        t_end = time.perf_counter() + 6.0
+        while len(runs) < 3 or (time.perf_counter() < t_end and len(runs) < 7):
+            t0 = time.perf_counter()
+            want = oracle.reduce(xs, threads=threads)
+            runs.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        oracle.reduce([x[: case.k // 16] for x in xs], threads=1)
+        single = (time.perf_counter() - t0) * 16
+        med = statistics.median(runs)
+        out["cpu_baseline"] = {
+            "value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full headline call (8 x 64 MiB in, 64 MiB out), median of {len(runs)} runs, "
+                      f"{threads} threads split by element range; single-thread estimate "
+                      f"{nbytes / single / 1e9:.3f} GB/s from 1/16 of the elements",
+            "ms": round(med * 1e3, 2),
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+        if not args.no_parity:
+            ok = bool(np.array_equal(got, want))
+            out.setdefault("parity", {})["headline"] = ok
+            log("headline parity", ok)
+    return ms, ach
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def run_c1(d, B, synth, oracle, args, out):
+    case = synth.C1_ONESHOT_8K
+    xs = case.inputs()
+    ins = [d.up(x) for x in xs]
+    res = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
+    t = timing(d, lambda: B.pc_reduce(ins, res, case.k), 2000, 100)
+    t.update(workload=case.name, bytes_per_call=case.bytes_moved(),
+             gbs_cache_resident=round(gbs(case.bytes_moved(), t["kernel_us"]), 1))
+    out["configs"]["oneshot_8k"] = t
+    if oracle is not None:
+        out["parity"]["oneshot_8k"] = bool(np.array_equal(d.down(res, np.uint16), oracle.reduce(xs)))
+
+
+def run_c2(d, B, synth, oracle, args, out):
+    torch = d.torch
+    case = synth.C2_LL_128K
+    pays, stales, masks = case.payloads(), case.stale_payloads(), case.stale_masks()
+    src = [d.up(x) for x in pays]
+    old_src = [d.up(s) for s in stales]
+    cur = [torch.empty(case.lines, dtype=torch.int64, device=d.dev) for _ in range(case.n)]
+    old = [torch.empty(case.lines, dtype=torch.int64, device=d.dev) for _ in range(case.n)]
+    for r in range(case.n):
+        B.pc_pack_ll(src[r], cur[r], case.k, case.seq)
+        B.pc_pack_ll(old_src[r], old[r], case.k, case.stale_seq)
+    staged = [torch.where(torch.from_numpy(m).to(d.dev), o, c) for m, o, c in zip(masks, old, cur)]
+    res = torch.full((case.k,), -1, dtype=torch.int16, device=d.dev)
+    bm = torch.empty(case.k // 128, dtype=torch.int64, device=d.dev)
+    tc = timing(d, lambda: B.pc_consume_ll(staged, res, case.k, case.seq, bm), 2000, 100)
+    tp = timing(d, lambda: B.pc_pack_ll(src[0], cur[0], case.k, case.seq), 2000, 100)
+    bits = d.down(bm, np.uint64)
+    ready = int(np.unpackbits(bits.view(np.uint8)).sum())
+    cbytes = case.n * case.lines * 8 + 4 * ready + case.lines // 8
+    tc.update(workload=case.name, ready_lines=ready, bytes_per_call=cbytes,
+              gbs_cache_resident=round(gbs(cbytes, tc["kernel_us"]), 1))
+    tp.update(workload="LL pack of one rank, 128 KiB -> 256 KiB", bytes_per_call=6 * case.k,
+              gbs_cache_resident=round(gbs(6 * case.k, tp["kernel_us"]), 1))
+    out["configs"]["ll_consume_128k"] = tc
+    out["configs"]["ll_pack_128k"] = tp
+    if oracle is not None:
+        for r in range(case.n):
+            B.pc_pack_ll(src[r], cur[r], case.k, case.seq)
+        host = [np.where(m, oracle.pack_ll(s, case.stale_seq), oracle.pack_ll(x, case.seq))
+                for x, s, m in zip(pays, stales, masks)]
+        ok_lines = all(np.array_equal(d.down(a, np.uint64), b) for a, b in zip(staged, host))
+        res.fill_(-1)
+        B.pc_consume_ll(staged, res, case.k, case.seq, bm)
+        wo, wb = oracle.consume_ll(host, case.k, case.seq)
+        out["parity"]["ll_128k"] = bool(ok_lines and np.array_equal(d.down(res, np.uint16), wo)
+                                        and np.array_equal(d.down(bm, np.uint64), wb))
+
+
+def run_c3(d, B, synth, oracle, args, out):
+    case = synth.C3_TWOSHOT_1M
+    xs = case.inputs()
+    ins = [d.up(x) for x in xs]
+    outs = [d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev) for _ in xs]
+    t = timing(d, lambda: B.pc_twoshot(ins, outs, case.k), 1000, 50)
+    nbytes = 2 * case.k * (2 * case.n + 1)
+    t.update(workload=case.name, bytes_per_call=nbytes,
+             gbs_cache_resident=round(gbs(nbytes, t["kernel_us"]), 1))
+    out["configs"]["twoshot_1m"] = t
+    if oracle is not None:
+        want = oracle.twoshot(xs)
+        one = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
+        B.pc_reduce(ins, one, case.k)
+        onev = d.down(one, np.uint16)
+        out["parity"]["twoshot_1m"] = bool(all(np.array_equal(d.down(o, np.uint16), w) and
+                                               np.array_equal(w, onev) for o, w in zip(outs, want)))
+
+
+def run_c5(d, B, synth, oracle, args, out):
+    case = synth.C5_ALLGATHER_2M
+    recs, masks = case.records()
+    shards = [d.up(r) for r in recs]
+    res = d.torch.full((case.n * case.shard_bytes // 2,), -1, dtype=d.torch.int16, device=d.dev)
+    bm = d.torch.empty(case.n * case.blocks // 64, dtype=d.torch.int64, device=d.dev)
+    t = timing(d, lambda: B.pc_allgather_copy(shards, res, case.shard_bytes, case.seq, bm), 1000, 50)
+    ready = int(sum((~m).sum() for m in masks))
+    nbytes = case.n * case.blocks * 136 + ready * 128 + case.n * case.blocks // 8
+    t.update(workload=case.name, ready_blocks=ready, bytes_per_call=nbytes,
+             gbs_cache_resident=round(gbs(nbytes, t["kernel_us"]), 1))
+    out["configs"]["allgather_2m"] = t
+    if oracle is not None:
+        wo, wb = oracle.allgather_copy(recs, case.shard_bytes, case.seq)
+        out["parity"]["allgather_2m"] = bool(np.array_equal(d.down(res, np.uint16), wo) and
+                                             np.array_equal(d.down(bm, np.uint64), wb))
+
+
+def run_sweep(d, B, synth, oracle, args, out):
+    rows = []
+    for nbytes in synth.SWEEP_BYTES:
+        k = nbytes // 2
+        for kind, n in (("reduce", 4), ("reduce", 8), ("twoshot", 8)):
+            xs = [synth.uniform_bf16(20, 0, r, k) for r in range(n)]
+            ins = [d.up(x) for x in xs]
+            if kind == "reduce":
+                res = d.torch.empty(k, dtype=d.torch.int16, device=d.dev)
+                fn = lambda: B.pc_reduce(ins, res, k)  # noqa: E731
+                moved = (n + 1) * nbytes
+            else:
+                outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
+                fn = lambda: B.pc_twoshot(ins, outs, k)  # noqa: E731
+                moved = (2 * n + 1) * nbytes
+            t = timing(d, fn, 500, 50)
+            row = {"call": kind, "n": n, "bytes_per_rank": nbytes, **t,
+                   "gbs_cache_resident": round(gbs(moved, t["kernel_us"]), 1)}
+            if oracle is not None:
+                want = oracle.reduce(xs)
+                got = d.down(res if kind == "reduce" else outs[n - 1], np.uint16)
+                row["parity"] = bool(np.array_equal(got, want))
+            rows.append(row)
+    out["latency_sweep"] = rows
+
+
+def run_floor(d, out):
+    torch = d.torch
+    fn = lambda: torch.cuda._sleep(0)  # noqa: E731
+    out["empty_kernel_floor"] = timing(d, fn, 2000, 100)
+
+
+def run_copy(d, out, steps):
+    """Plain device-to-device copy of 256 MiB (calibration for HBM counters)."""
+    torch = d.torch
+    a = torch.empty(128 << 20, dtype=torch.int16, device=d.dev).fill_(1)
+    b = torch.empty_like(a)
+    ms = d.events_ms(lambda: b.copy_(a), steps, 5)
+    out["copy_256m"] = {"kernel_us": round(ms * 1e3, 3), "bytes_per_call": 2 * (256 << 20),
+                        "gbs": round(gbs(2 * (256 << 20), ms * 1e3), 1)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the datapath on one GPU; multi-GPU runs "
+              "are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from collective_datapath_amd import binding as B
+    from collective_datapath_amd import synth
+    d = Dev()
+    out = {"configs": {}, "parity": {}}
+    oracle = None
+    if not args.no_parity:
+        import oracle as _oracle
+        oracle = _oracle
+    t0 = time.time()
+
+    headline_ms = ach = None
+    if args.only in ("all", "headline"):
+        headline_ms, ach = run_headline(d, B, synth, args, out)
+    if args.only == "copy":
+        run_copy(d, out, args.steps)
+    for name, fn in (("c1", run_c1), ("c2", run_c2), ("c3", run_c3), ("c5", run_c5),
+                     ("sweep", run_sweep)):
+        if args.only in ("all", name):
+            log("running", name)
+            fn(d, B, synth, oracle, args, out)
+    if args.only == "all":
+        run_floor(d, out)
+    log(f"done in {time.time() - t0:.1f} s")
+
+    line = {"metric": METRIC, "value": round(ach, 1) if ach else None, "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(headline_ms, 5) if headline_ms else None,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "oneshot reduce, N=8 ranks, K=4096x8192 bf16 (64 MiB/rank), "
+                                   "normal(0,0.02), fp32 accumulate in rank order 0..7, bf16 RNE output",
+                       "n": 8, "k": 4096 * 8192, "bytes_per_call": 9 * 2 * 4096 * 8192}}
+    if ach:
+        line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "pcdp::k_reduce<8, 4, true, false>"}
+    if "cpu_baseline" in out:
+        line["cpu_baseline"] = out.pop("cpu_baseline")
+    line.update(out)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+"""Thin Python binding of libpcdp.so (the C ABI in include/pc.h).
+
+Argument marshalling only: device buffers are torch tensors (or raw device
+addresses as ints), host pointer arrays are built here, and every call goes
+straight to the HIP library, which does all the work.  There is no fallback:
+if the built library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpcdp.so")
+
+PC_OK, PC_EINVAL, PC_EALIGN, PC_EUNSUPPORTED, PC_EHIP = 0, -1, -2, -3, -4
+PC_MAX_RANKS = 8
+PC_LL_LINE_BYTES = 8
+PC_BLOCK_PAYLOAD_BYTES = 128
+PC_BLOCK_RECORD_BYTES = 136
+
+# Every symbol include/pc.h declares.
+EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_allgather_copy",
+           "pc_strerror", "pc_abi_version")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python collective_datapath_amd/build.py` first")
+
+# torch owns device memory and streams, so the library must run on torch's HIP
+# runtime.  Loading torch first makes the dynamic linker resolve the library's
+# libamdhip64.so.7 to the runtime torch already mapped; loading the library
+# first would map a second runtime whose view of streams and allocations is
+# disjoint from torch's.
+import torch  # noqa: E402,F401
+
+
+def _hip_runtimes():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are mapped in this process "
+                      f"({sorted(_hip_runtimes())}); import torch before loading libpcdp.so")
+_P, _S, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_lib.pc_reduce.argtypes = [_P, _I, _P, _S, _P, _P]
+_lib.pc_pack_ll.argtypes = [_P, _P, _S, ctypes.c_uint32, _P]
+_lib.pc_consume_ll.argtypes = [_P, _I, _P, _S, ctypes.c_uint32, _P, _P]
+_lib.pc_twoshot.argtypes = [_P, _I, _P, _S, _P]
+_lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
+for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_allgather_copy"):
+    getattr(_lib, _f).restype = _I
+_lib.pc_strerror.argtypes = [_I]
+_lib.pc_strerror.restype = ctypes.c_char_p
+_lib.pc_abi_version.restype = _I
+
+Buffer = Union[int, "torch.Tensor"]  # noqa: F821
+
+
+class PCError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {pc_strerror(status)} (status {status})")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _addr(b: Optional[Buffer]) -> int:
+    if b is None:
+        return 0
+    if isinstance(b, int):
+        return b
+    return b.data_ptr()
+
+
+def _addrs(bs: Sequence[Buffer]):
+    return (ctypes.c_void_p * max(len(bs), 1))(*[_addr(b) for b in bs])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _call(fn: str, status: int, check: bool) -> int:
+    if check and status != PC_OK:
+        raise PCError(fn, status)
+    return status
+
+
+def pc_strerror(status: int) -> str:
+    return _lib.pc_strerror(status).decode()
+
+
+def pc_abi_version() -> int:
+    return _lib.pc_abi_version()
+
+
+def pc_reduce(inputs: Sequence[Buffer], out: Buffer, k: int, order: Optional[Sequence[int]] = None,
+              stream=None, check: bool = True) -> int:
+    if order is not None and len(order) != len(inputs):
+        raise ValueError("order must list every rank exactly once")
+    ordp = (ctypes.c_int32 * len(order))(*order) if order is not None else None
+    st = _lib.pc_reduce(_addrs(inputs), len(inputs), _addr(out), k,
+                        ctypes.cast(ordp, ctypes.c_void_p) if ordp is not None else None,
+                        _stream(stream))
+    return _call("pc_reduce", st, check)
+
+
+def pc_pack_ll(src: Buffer, dst: Buffer, k: int, seq: int, stream=None, check: bool = True) -> int:
+    st = _lib.pc_pack_ll(_addr(src), _addr(dst), k, seq, _stream(stream))
+    return _call("pc_pack_ll", st, check)
+
+
+def pc_consume_ll(lines: Sequence[Buffer], out: Buffer, k: int, seq: int, ready_bitmap: Buffer,
+                  stream=None, check: bool = True) -> int:
+    st = _lib.pc_consume_ll(_addrs(lines), len(lines), _addr(out), k, seq, _addr(ready_bitmap),
+                            _stream(stream))
+    return _call("pc_consume_ll", st, check)
+
+
+def pc_twoshot(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=None,
+               check: bool = True) -> int:
+    if len(outs) != len(inputs):
+        raise ValueError("pc_twoshot needs one output per input")
+    st = _lib.pc_twoshot(_addrs(inputs), len(inputs), _addrs(outs), k, _stream(stream))
+    return _call("pc_twoshot", st, check)
+
+
+def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, seq: int,
+                      ready_bitmap: Buffer, stream=None, check: bool = True) -> int:
+    st = _lib.pc_allgather_copy(_addrs(shards), len(shards), _addr(out), shard_bytes, seq,
+                                _addr(ready_bitmap), _stream(stream))
+    return _call("pc_allgather_copy", st, check)

@@ -1,0 +1,165 @@
+// pc_api.hip -- the C ABI declared in include/pc.h: argument validation, the
+// fold-order permutation, and dispatch to the kernel launchers.
+//
+// Admission follows the spirit of "flash-comm: Self-Synchronizing Collective
+// Communication for LLM Decoding", Section 4.1: a call is checked before
+// anything is launched (group size, 16-byte address and length alignment,
+// size ceiling), and a rejected call has no side effect.  Empty payloads are
+// legal no-ops so that every rank can issue the same call sequence
+// (Section 4.2).  Nothing here allocates or keeps state.
+#include "../../include/pc.h"
+#include "pc_launch.hpp"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+inline bool valid_n(int n) { return n >= 1 && n <= PC_MAX_RANKS; }
+
+bool is_permutation(const int32_t* order, int n) {
+    bool seen[PC_MAX_RANKS] = {};
+    for (int j = 0; j < n; ++j) {
+        const int32_t r = order[j];
+        if (r < 0 || r >= n || seen[r]) return false;
+        seen[r] = true;
+    }
+    return true;
+}
+
+// Every pointer non-null (PC_EINVAL) and 16-byte aligned (PC_EALIGN).
+template <typename T>
+pc_status check_ptrs(const T* const* ptrs, int n) {
+    for (int r = 0; r < n; ++r)
+        if (!ptrs[r]) return PC_EINVAL;
+    for (int r = 0; r < n; ++r)
+        if (!aligned16(ptrs[r])) return PC_EALIGN;
+    return PC_OK;
+}
+
+inline pc_status from_hip(hipError_t e) { return e == hipSuccess ? PC_OK : PC_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t k,
+                    const int32_t* order, void* stream) {
+    if (!valid_n(n) || !inputs) return PC_EINVAL;
+    if (order && !is_permutation(order, n)) return PC_EINVAL;
+    if (k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (k % 8) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (pc_status st = check_ptrs(inputs, n)) return st;
+    if (!out) return PC_EINVAL;
+    if (!aligned16(out)) return PC_EALIGN;
+    const size_t bytes = k * sizeof(uint16_t);
+    for (int r = 0; r < n; ++r)
+        if (inputs[r] != out && overlaps(inputs[r], bytes, out, bytes)) return PC_EINVAL;
+    const void* src[PC_MAX_RANKS];
+    for (int j = 0; j < n; ++j) src[j] = inputs[order ? order[j] : j];
+    return from_hip(pcdp::launch_reduce(src, n, out, k / 8, static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32_t seq, void* stream) {
+    if (seq == 0 || k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (k % 8) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (!src || !dst) return PC_EINVAL;
+    if (!aligned16(src) || !aligned16(dst)) return PC_EALIGN;
+    if (overlaps(src, k * sizeof(uint16_t), dst, (k / 2) * sizeof(uint64_t))) return PC_EINVAL;
+    return from_hip(pcdp::launch_pack_ll(src, dst, k / 8, seq, static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* out, size_t k,
+                        uint32_t seq, uint64_t* ready_bitmap, void* stream) {
+    if (!valid_n(n) || !lines || seq == 0 || k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (k % 128) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (pc_status st = check_ptrs(lines, n)) return st;
+    if (!out || !ready_bitmap) return PC_EINVAL;
+    if (!aligned16(out) || !aligned16(ready_bitmap)) return PC_EALIGN;
+    const size_t nlines = k / 2;
+    const size_t line_bytes = nlines * sizeof(uint64_t);
+    const size_t out_bytes = k * sizeof(uint16_t);
+    const size_t bm_bytes = (nlines / 64) * sizeof(uint64_t);
+    if (overlaps(out, out_bytes, ready_bitmap, bm_bytes)) return PC_EINVAL;
+    for (int r = 0; r < n; ++r)
+        if (overlaps(lines[r], line_bytes, out, out_bytes) ||
+            overlaps(lines[r], line_bytes, ready_bitmap, bm_bytes))
+            return PC_EINVAL;
+    const void* src[PC_MAX_RANKS];
+    for (int r = 0; r < n; ++r) src[r] = lines[r];
+    return from_hip(pcdp::launch_consume_ll(src, n, out, nlines, seq, ready_bitmap,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
+                     void* stream) {
+    if (!valid_n(n) || !inputs || !outs || k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (k % (8 * (size_t)n)) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (pc_status st = check_ptrs(inputs, n)) return st;
+    if (pc_status st = check_ptrs(outs, n)) return st;
+    const size_t bytes = k * sizeof(uint16_t);
+    for (int a = 0; a < n; ++a) {
+        for (int b = a + 1; b < n; ++b)
+            if (overlaps(outs[a], bytes, outs[b], bytes)) return PC_EINVAL;
+        for (int r = 0; r < n; ++r)
+            if (inputs[r] != outs[a] && overlaps(inputs[r], bytes, outs[a], bytes)) return PC_EINVAL;
+    }
+    const void* src[PC_MAX_RANKS];
+    void* dst[PC_MAX_RANKS];
+    for (int r = 0; r < n; ++r) {
+        src[r] = inputs[r];
+        dst[r] = outs[r];
+    }
+    return from_hip(pcdp::launch_twoshot(src, n, dst, k / 8 / (size_t)n,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
+                            size_t shard_bytes, uint64_t seq, uint64_t* ready_bitmap,
+                            void* stream) {
+    if (!valid_n(n) || !shards || seq == 0 || shard_bytes > 2 * PC_MAX_ELEMS) return PC_EINVAL;
+    if (shard_bytes % 8192) return PC_EALIGN;
+    if (shard_bytes == 0) return PC_OK;
+    if (pc_status st = check_ptrs(shards, n)) return st;
+    if (!out || !ready_bitmap) return PC_EINVAL;
+    if (!aligned16(out) || !aligned16(ready_bitmap)) return PC_EALIGN;
+    const size_t blocks = shard_bytes / PC_BLOCK_PAYLOAD_BYTES;
+    const size_t rec_bytes = blocks * PC_BLOCK_RECORD_BYTES;
+    const size_t out_bytes = (size_t)n * shard_bytes;
+    const size_t bm_bytes = (size_t)n * blocks / 64 * sizeof(uint64_t);
+    if (overlaps(out, out_bytes, ready_bitmap, bm_bytes)) return PC_EINVAL;
+    for (int r = 0; r < n; ++r)
+        if (overlaps(shards[r], rec_bytes, out, out_bytes) ||
+            overlaps(shards[r], rec_bytes, ready_bitmap, bm_bytes))
+            return PC_EINVAL;
+    const void* src[PC_MAX_RANKS];
+    for (int r = 0; r < n; ++r) src[r] = shards[r];
+    return from_hip(pcdp::launch_allgather(src, n, out, blocks / 64, seq, ready_bitmap,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+const char* pc_strerror(pc_status status) {
+    switch (status) {
+        case PC_OK: return "success";
+        case PC_EINVAL: return "invalid argument";
+        case PC_EALIGN: return "misaligned pointer or size";
+        case PC_EUNSUPPORTED: return "unsupported";
+        case PC_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int pc_abi_version(void) { return PC_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// pc_device.hpp -- device-side building blocks of the gfx950 datapath kernels.
+//
+// Element arithmetic follows "Purlin: Separating Orchestration from the
+// Datapath of Collectives", Section 3.3, Equation (2): every bf16 contribution
+// is widened to fp32, contributions are added in a fixed rank order in fp32,
+// and the finished sum is rounded back to bf16.  Rounding is to nearest,
+// ties to even; every NaN becomes the canonical quiet NaN 0x7FC0, so a NaN
+// result has exactly one bit pattern whichever operand's payload the adder
+// would have kept.  Subnormals are kept: the library is compiled with
+// -fno-gpu-flush-denormals-to-zero and without contraction.
+//
+// Memory is moved in 16-byte units (global_load_dwordx4 / global_store_dwordx4)
+// so that a wave64 touches 1 KiB contiguous per instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pcdp {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxRanks = 8;
+constexpr int kWave = 64;
+
+// Pointer bundles passed by value as kernel arguments (they live in SGPRs).
+template <typename T>
+struct Ptrs {
+    T p[kMaxRanks];
+};
+
+// ---- loads and stores -------------------------------------------------------
+// Streaming (non-temporal) variants are used when the working set is far
+// larger than the caches, so one pass does not evict data that is reused.
+template <bool kStream>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+    if constexpr (kStream) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool kStream>
+__device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
+    if constexpr (kStream) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// ---- bf16 <-> fp32 ----------------------------------------------------------
+// A 32-bit word holds two bf16: element 2i in bits 0..15, element 2i+1 in
+// bits 16..31.  Widening is exact: the bf16 bits become the upper fp32 half.
+__device__ __forceinline__ float widen_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float widen_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 rounded to nearest even, left in the upper 16 bits of the
+// returned word (the lower 16 bits are junk).  Adding 0x7FFF plus the kept
+// value's lowest bit rounds ties to even; a carry into the exponent is the
+// right answer and carries out of the largest finite value give +-Inf.
+__device__ __forceinline__ uint32_t round_bf16_hi(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC00000u : r;
+}
+
+// Two fp32 sums -> one word of two bf16 (lo -> bits 0..15, hi -> 16..31).
+__device__ __forceinline__ uint32_t narrow_pair(float lo, float hi) {
+    return (round_bf16_hi(hi) & 0xFFFF0000u) | (round_bf16_hi(lo) >> 16);
+}
+
+// ---- the rank-ordered fold of one 16-byte chunk -------------------------------
+// v[r] holds 8 bf16 of rank r's chunk; the result holds the 8 sums.  Each of
+// the 8 lanes-within-the-chunk has its own accumulator that starts at -0.0f
+// and takes ranks 0, 1, ..., N-1 in that order; no term is ever combined with
+// another before it reaches the accumulator.
+template <int N>
+__device__ __forceinline__ u32x4 fold_chunk(const u32x4 (&v)[N]) {
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = -0.0f;
+        hi[e] = -0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo[e] = lo[e] + widen_lo(v[r][e]);
+            hi[e] = hi[e] + widen_hi(v[r][e]);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = narrow_pair(lo[e], hi[e]);
+    return o;
+}
+
+}  // namespace pcdp

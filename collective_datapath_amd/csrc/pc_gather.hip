@@ -1,0 +1,76 @@
+// pc_gather.hip -- all-gather copy of sequence-stamped 128-byte blocks.
+//
+// "flash-comm: Self-Synchronizing Collective Communication for LLM
+// Decoding", Section 4.3 (all-gather: each source publishes one shard and
+// receivers take each shard through the same readiness layer, with no
+// reduction) and Section 3.1 (a unit is accepted only when its sequence
+// number matches the current call); Appendix A, Table 8 discussion (128-byte
+// writes were never observed torn).  "Purlin: Separating Orchestration from
+// the Datapath of Collectives", Section 3.1 (AllGather places the gathered
+// partitions in rank order).
+//
+// A shard is an array of 136-byte records: a u64 sequence header followed by
+// 128 payload bytes.  136 is not a multiple of 16, so every other payload
+// starts 8 bytes off a 16-byte boundary.  A workgroup therefore stages 64
+// records (8704 bytes = 544 aligned 16-byte pieces, one bitmap word) in LDS
+// with coalesced 16-byte loads, then writes the accepted payloads to the
+// output with coalesced 16-byte stores; LDS does the repacking.
+#include "pc_device.hpp"
+#include "pc_launch.hpp"
+
+namespace pcdp {
+
+constexpr int kGBlock = 256;
+constexpr int kGroup = 64;                      // records per workgroup = one bitmap word
+constexpr int kRecBytes = 136;
+constexpr int kGroupPieces = kGroup * kRecBytes / 16;  // 544
+
+// Grid: x = group within a shard, y = shard.
+__global__ __launch_bounds__(kGBlock) void k_allgather(Ptrs<const u32x4*> shards, u32x4* out,
+                                                        uint64_t* bitmap, uint64_t seq,
+                                                        uint32_t groups) {
+    __shared__ u32x4 tile[kGroupPieces];
+    const uint32_t g = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+    const u32x4* src = shards.p[r] + (size_t)g * kGroupPieces;
+    for (uint32_t c = t; c < (uint32_t)kGroupPieces; c += kGBlock) tile[c] = src[c];
+    __syncthreads();
+
+    const unsigned char* bytes = reinterpret_cast<const unsigned char*>(tile);
+    const size_t item0 = ((size_t)r * groups + g) * kGroup;  // first output block of the group
+    u32x4* dst = out + item0 * 8;
+    // 64 records x 8 pieces of 16 bytes; consecutive lanes take consecutive pieces.
+#pragma unroll
+    for (int k = 0; k < kGroup * 8 / kGBlock; ++k) {
+        const uint32_t q = k * kGBlock + t;
+        const uint32_t i = q >> 3, piece = q & 7;
+        const unsigned char* rec = bytes + i * kRecBytes;
+        const uint64_t hdr = *reinterpret_cast<const uint64_t*>(rec);
+        if (hdr == seq) {
+            const uint64_t* p8 = reinterpret_cast<const uint64_t*>(rec + 8 + 16 * piece);
+            const uint64_t a = p8[0], b = p8[1];
+            u32x4 v;
+            v[0] = (uint32_t)a; v[1] = (uint32_t)(a >> 32);
+            v[2] = (uint32_t)b; v[3] = (uint32_t)(b >> 32);
+            dst[q] = v;
+        }
+    }
+    if (t < kWave) {
+        const uint64_t hdr = *reinterpret_cast<const uint64_t*>(bytes + t * kRecBytes);
+        const uint64_t word = __ballot(hdr == seq);
+        if (t == 0) bitmap[item0 / kGroup] = word;
+    }
+}
+
+hipError_t launch_allgather(const void* const* shards, int n, void* out, size_t groups,
+                            uint64_t seq, void* bitmap, hipStream_t stream) {
+    Ptrs<const u32x4*> p;
+    for (int r = 0; r < kMaxRanks; ++r) p.p[r] = r < n ? static_cast<const u32x4*>(shards[r]) : nullptr;
+    u32x4* o = static_cast<u32x4*>(out);
+    uint64_t* b = static_cast<uint64_t*>(bitmap);
+    uint32_t gr = (uint32_t)groups;
+    dim3 grid(gr, (unsigned)n);
+    void* args[] = {&p, &o, &b, &seq, &gr};
+    return hipLaunchKernel((const void*)&k_allgather, grid, dim3(kGBlock), args, 0, stream);
+}
+
+}  // namespace pcdp

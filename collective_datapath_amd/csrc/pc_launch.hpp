@@ -1,0 +1,37 @@
+// pc_launch.hpp -- host-side launchers of the datapath kernels.
+//
+// Arguments reaching a launcher have been validated by the C ABI layer
+// (pc_api.hip): pointers non-null and 16-byte aligned, sizes in range and
+// multiples of the kernel's unit, n in 1..8.  Each launcher enqueues its
+// kernel(s) on `stream` and returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pcdp {
+
+// out[c] = fold over ranks of src[r][c], for 16-byte chunks c < nchunks.
+// src has n pointers already permuted into fold order.
+hipError_t launch_reduce(const void* const* src, int n, void* out, size_t nchunks,
+                         hipStream_t stream);
+
+// Twoshot: slice s (nchunks_slice 16-byte chunks) folded into outs[s], then
+// copied from outs[s] into every outs[r], r != s.
+hipError_t launch_twoshot(const void* const* src, int n, void* const* outs,
+                          size_t nchunks_slice, hipStream_t stream);
+
+// LL lines: 16-byte chunks of src -> 4 lines each.
+hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t seq,
+                          hipStream_t stream);
+
+// LL consume over nlines lines (a multiple of 64).
+hipError_t launch_consume_ll(const void* const* lines, int n, void* out, size_t nlines,
+                             uint32_t seq, void* bitmap, hipStream_t stream);
+
+// All-gather of n shards of `groups` 64-record groups each.
+hipError_t launch_allgather(const void* const* shards, int n, void* out, size_t groups,
+                            uint64_t seq, void* bitmap, hipStream_t stream);
+
+}  // namespace pcdp

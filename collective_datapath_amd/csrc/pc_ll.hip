@@ -1,0 +1,128 @@
+// pc_ll.hip -- sequence-number ("LL") lines: pack on the producer side,
+// validate-and-fold on the consumer side.
+//
+// "flash-comm: Self-Synchronizing Collective Communication for LLM
+// Decoding", Section 3.1 (sequence-number readiness: data and the call's
+// sequence number travel in one transfer unit; a receiver accepts the data
+// only when the number matches the current call), Section 4.3 (16-byte
+// packet = 8 payload bytes + two copies of the sequence number; one-hop
+// reduce only after every source is ready, folded by source rank in rank
+// order) and Section 3.3 (fold order 0..N-1).  "Purlin: Separating
+// Orchestration from the Datapath of Collectives", Section 3.2 (latency path:
+// payload packed with a flag so the consumer polls the data itself).
+//
+// Line j (8 bytes, little-endian): bytes 0..3 = bf16 elements 2j (low half)
+// and 2j+1 (high half), bytes 4..7 = sequence number.  Two lines make one of
+// flash-comm's 16-byte packets.  Each line is read with one 8-byte load, so
+// its data and its sequence number are observed together.
+#include "pc_device.hpp"
+#include "pc_launch.hpp"
+
+namespace pcdp {
+
+constexpr int kLLBlock = 256;
+constexpr int kLLWaves = kLLBlock / kWave;
+
+// ---- pack: 8 bf16 (16 bytes) in -> 4 lines (32 bytes) out -----------------------
+template <int U>
+__global__ __launch_bounds__(kLLBlock) void k_pack_ll(const u32x4* src, u32x4* dst, uint32_t seq,
+                                                       size_t nchunks) {
+    const size_t tile0 = (size_t)blockIdx.x * (kLLBlock * U);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t c = tile0 + u * kLLBlock + threadIdx.x;
+        if (c < nchunks) {
+            const u32x4 v = src[c];
+            u32x4 a, b;
+            a[0] = v[0]; a[1] = seq; a[2] = v[1]; a[3] = seq;
+            b[0] = v[2]; b[1] = seq; b[2] = v[3]; b[3] = seq;
+            dst[2 * c] = a;
+            dst[2 * c + 1] = b;
+        }
+    }
+}
+
+// ---- consume: every wave owns U groups of 64 consecutive lines ------------------
+// Lane l of group u takes line base + 64u + l from every rank.  The wave's
+// ballot over "all ranks carry seq" is exactly the 64-bit bitmap word of the
+// group (bit l = line base + 64u + l), so no bit shuffling is needed.  Lines
+// that are ready are folded in rank order and stored; the rest are skipped,
+// leaving their output as it was.
+template <int N, int U>
+__global__ __launch_bounds__(kLLBlock) void k_consume_ll(Ptrs<const u32x2*> lines, uint32_t* out,
+                                                          uint64_t* bitmap, uint32_t seq,
+                                                          size_t nlines) {
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = threadIdx.x / kWave;
+    const size_t base = ((size_t)blockIdx.x * kLLWaves + wave) * (kWave * U);
+    if (base >= nlines) return;  // whole wave past the end
+    u32x2 l[U][N];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (base + (size_t)u * kWave < nlines) {
+#pragma unroll
+            for (int r = 0; r < N; ++r) l[u][r] = lines.p[r][base + u * kWave + lane];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t g = base + (size_t)u * kWave;
+        if (g >= nlines) break;
+        bool ready = true;
+#pragma unroll
+        for (int r = 0; r < N; ++r) ready = ready && (l[u][r][1] == seq);
+        const uint64_t word = __ballot(ready);
+        if (ready) {
+            float lo = -0.0f, hi = -0.0f;
+#pragma unroll
+            for (int r = 0; r < N; ++r) {
+                lo = lo + widen_lo(l[u][r][0]);
+                hi = hi + widen_hi(l[u][r][0]);
+            }
+            out[g + lane] = narrow_pair(lo, hi);
+        }
+        if (lane == 0) bitmap[g / kWave] = word;
+    }
+}
+
+hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t seq,
+                          hipStream_t stream) {
+    constexpr int U = 2;
+    const size_t tile = (size_t)kLLBlock * U;
+    dim3 grid((unsigned)((nchunks + tile - 1) / tile));
+    const u32x4* s = static_cast<const u32x4*>(src);
+    u32x4* d = static_cast<u32x4*>(dst);
+    void* args[] = {&s, &d, &seq, &nchunks};
+    return hipLaunchKernel((const void*)&k_pack_ll<U>, grid, dim3(kLLBlock), args, 0, stream);
+}
+
+template <int N>
+static hipError_t go_consume(Ptrs<const u32x2*> p, uint32_t* out, uint64_t* bitmap, uint32_t seq,
+                             size_t nlines, hipStream_t stream) {
+    constexpr int U = 2;
+    const size_t per_block = (size_t)kLLWaves * kWave * U;
+    dim3 grid((unsigned)((nlines + per_block - 1) / per_block));
+    void* args[] = {&p, &out, &bitmap, &seq, &nlines};
+    return hipLaunchKernel((const void*)&k_consume_ll<N, U>, grid, dim3(kLLBlock), args, 0, stream);
+}
+
+hipError_t launch_consume_ll(const void* const* lines, int n, void* out, size_t nlines,
+                             uint32_t seq, void* bitmap, hipStream_t stream) {
+    Ptrs<const u32x2*> p;
+    for (int r = 0; r < kMaxRanks; ++r) p.p[r] = r < n ? static_cast<const u32x2*>(lines[r]) : nullptr;
+    uint32_t* o = static_cast<uint32_t*>(out);
+    uint64_t* b = static_cast<uint64_t*>(bitmap);
+    switch (n) {
+        case 1: return go_consume<1>(p, o, b, seq, nlines, stream);
+        case 2: return go_consume<2>(p, o, b, seq, nlines, stream);
+        case 3: return go_consume<3>(p, o, b, seq, nlines, stream);
+        case 4: return go_consume<4>(p, o, b, seq, nlines, stream);
+        case 5: return go_consume<5>(p, o, b, seq, nlines, stream);
+        case 6: return go_consume<6>(p, o, b, seq, nlines, stream);
+        case 7: return go_consume<7>(p, o, b, seq, nlines, stream);
+        case 8: return go_consume<8>(p, o, b, seq, nlines, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pcdp

@@ -1,0 +1,195 @@
+// pc_reduce.hip -- the rank-ordered N-way reduce and the twoshot split.
+//
+// Reduce: "Purlin: Separating Orchestration from the Datapath of
+// Collectives", Section 3.3 (the Atom's reduce of n typed sources, Equation
+// (2)); oneshot's local reduction in "SiFAR: Synchronization-Free All-Reduce
+// for Low-Latency LLM Inference", Section 3.1, Figure 5.
+// Twoshot: SiFAR Section 3.1, Figure 6 (reduce-scatter, then broadcast) and
+// "flash-comm: Self-Synchronizing Collective Communication for LLM
+// Decoding", Section 3.3 (one owner reduces each block once and distributes
+// it) and Section 4.3 (sharded two-hop).
+//
+// Work mapping.  Each 16-byte chunk (8 bf16) of the output belongs to one
+// lane; a 256-lane workgroup owns a tile of 256*U consecutive chunks, lane t
+// taking chunks t, t+256, ... so every load and store instruction of a wave
+// covers 1 KiB of consecutive bytes per rank.  All N*U loads of a lane are
+// issued before its first fold, which keeps N*U*16 bytes per lane in flight:
+// the gfx950 counterpart of sizing a copy pipeline to the bandwidth-delay
+// product (Purlin, Section 3.3, Equation (3)).  The tile count is far above
+// the 256 CUs for bandwidth-sized payloads, so every XCD streams.
+#include "pc_device.hpp"
+#include "pc_launch.hpp"
+
+namespace pcdp {
+
+constexpr int kBlock = 256;
+
+// ---- slice reduce (oneshot when there is one slice) ----------------------------
+// Grid: x = tile within a slice, y = slice.  Slice s covers chunks
+// [s*nslice, (s+1)*nslice) of every input and lands in dst.p[kSliced ? s : 0].
+template <int N, int U, bool kStream, bool kSliced>
+__global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
+                                                     uint32_t nslice) {
+    constexpr uint32_t kTile = kBlock * U;
+    const uint32_t s = kSliced ? blockIdx.y : 0u;
+    const uint32_t tile0 = blockIdx.x * kTile;
+    const size_t first = (size_t)s * nslice + tile0;
+    const uint32_t left = nslice - tile0;
+    const uint32_t t = threadIdx.x;
+    u32x4* out = dst.p[s] + first;
+    const u32x4* in[N];
+#pragma unroll
+    for (int r = 0; r < N; ++r) in[r] = src.p[r] + first;
+
+    if (left >= kTile) {
+        u32x4 v[U][N];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < N; ++r) v[u][r] = load16<kStream>(in[r] + u * kBlock + t);
+#pragma unroll
+        for (int u = 0; u < U; ++u) store16<kStream>(out + u * kBlock + t, fold_chunk<N>(v[u]));
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = u * kBlock + t;
+            if (c < left) {
+                u32x4 v[N];
+#pragma unroll
+                for (int r = 0; r < N; ++r) v[r] = load16<kStream>(in[r] + c);
+                store16<kStream>(out + c, fold_chunk<N>(v));
+            }
+        }
+    }
+}
+
+// ---- twoshot copy-out: the owner's slice goes to every other rank's output ----
+// Grid: x = tile within a slice, y = slice s.  Reads outs[s] once per chunk
+// and writes it to the N-1 other outputs.
+template <int N, int U>
+__global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t nslice) {
+    constexpr uint32_t kTile = kBlock * U;
+    const uint32_t s = blockIdx.y;
+    const uint32_t tile0 = blockIdx.x * kTile;
+    const size_t first = (size_t)s * nslice + tile0;
+    const uint32_t left = nslice - tile0;
+    const uint32_t t = threadIdx.x;
+    const u32x4* from = outs.p[s] + first;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t c = u * kBlock + t;
+        if (left >= kTile || c < left) v[u] = from[c];
+    }
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        if ((uint32_t)r == s) continue;
+        u32x4* to = outs.p[r] + first;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = u * kBlock + t;
+            if (left >= kTile || c < left) to[c] = v[u];
+        }
+    }
+}
+
+// ---- launch table ---------------------------------------------------------------
+// Shapes by payload: small payloads (latency regime, cache resident) take one
+// chunk per lane so the most workgroups start at once; mid payloads take two;
+// payloads whose working set is far beyond the 256 MiB of last-level cache
+// stream with non-temporal hints and four chunks per lane per rank.
+enum class Regime { kSmall, kMid, kStream };
+
+static Regime pick_regime(size_t nchunks_per_rank, int n) {
+    const size_t per_rank = nchunks_per_rank * 16;
+    const size_t working_set = per_rank * (size_t)(n + 1);
+    if (working_set >= ((size_t)192 << 20)) return Regime::kStream;
+    if (nchunks_per_rank >= (size_t)kBlock * 2 * 512) return Regime::kMid;
+    return Regime::kSmall;
+}
+
+template <int N, int U, bool kStream, bool kSliced>
+static hipError_t go_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                            uint32_t slices, hipStream_t stream) {
+    constexpr uint32_t kTile = kBlock * U;
+    dim3 grid((nslice + kTile - 1) / kTile, slices);
+    void* args[] = {&src, &dst, &nslice};
+    return hipLaunchKernel((const void*)&k_reduce<N, U, kStream, kSliced>, grid, dim3(kBlock), args,
+                           0, stream);
+}
+
+template <int N, bool kSliced>
+static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
+                                   uint32_t nslice, uint32_t slices, hipStream_t stream) {
+    switch (rg) {
+        case Regime::kStream: return go_reduce<N, 4, true, kSliced>(src, dst, nslice, slices, stream);
+        case Regime::kMid: return go_reduce<N, 2, false, kSliced>(src, dst, nslice, slices, stream);
+        default: return go_reduce<N, 1, false, kSliced>(src, dst, nslice, slices, stream);
+    }
+}
+
+template <bool kSliced>
+static hipError_t dispatch_reduce(int n, Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
+                                  uint32_t nslice, uint32_t slices, hipStream_t stream) {
+    switch (n) {
+        case 1: return go_reduce_regime<1, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 2: return go_reduce_regime<2, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 3: return go_reduce_regime<3, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 4: return go_reduce_regime<4, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 5: return go_reduce_regime<5, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 6: return go_reduce_regime<6, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 7: return go_reduce_regime<7, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 8: return go_reduce_regime<8, kSliced>(rg, src, dst, nslice, slices, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int N>
+static hipError_t go_copyout(Ptrs<u32x4*> outs, uint32_t nslice, uint32_t slices, bool wide,
+                             hipStream_t stream) {
+    if (wide) {
+        dim3 grid((nslice + 2 * kBlock - 1) / (2 * kBlock), slices);
+        void* args[] = {&outs, &nslice};
+        return hipLaunchKernel((const void*)&k_copyout<N, 2>, grid, dim3(kBlock), args, 0, stream);
+    }
+    dim3 grid((nslice + kBlock - 1) / kBlock, slices);
+    void* args[] = {&outs, &nslice};
+    return hipLaunchKernel((const void*)&k_copyout<N, 1>, grid, dim3(kBlock), args, 0, stream);
+}
+
+static void fill_src(Ptrs<const u32x4*>& p, const void* const* src, int n) {
+    for (int r = 0; r < kMaxRanks; ++r) p.p[r] = r < n ? static_cast<const u32x4*>(src[r]) : nullptr;
+}
+
+hipError_t launch_reduce(const void* const* src, int n, void* out, size_t nchunks,
+                         hipStream_t stream) {
+    Ptrs<const u32x4*> s;
+    Ptrs<u32x4*> d = {};
+    fill_src(s, src, n);
+    d.p[0] = static_cast<u32x4*>(out);
+    return dispatch_reduce<false>(n, pick_regime(nchunks, n), s, d, (uint32_t)nchunks, 1, stream);
+}
+
+hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size_t nchunks_slice,
+                          hipStream_t stream) {
+    Ptrs<const u32x4*> s;
+    Ptrs<u32x4*> d = {};
+    fill_src(s, src, n);
+    for (int r = 0; r < n; ++r) d.p[r] = static_cast<u32x4*>(outs[r]);
+    const Regime rg = pick_regime(nchunks_slice * (size_t)n, n);
+    hipError_t e = dispatch_reduce<true>(n, rg, s, d, (uint32_t)nchunks_slice, (uint32_t)n, stream);
+    if (e != hipSuccess || n == 1) return e;
+    const bool wide = rg != Regime::kSmall;
+    switch (n) {
+        case 2: return go_copyout<2>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 3: return go_copyout<3>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 4: return go_copyout<4>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 5: return go_copyout<5>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 6: return go_copyout<6>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 7: return go_copyout<7>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 8: return go_copyout<8>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pcdp

@@ -47,6 +47,12 @@
 extern "C" {
 #endif
 
+#if defined(__GNUC__)
+#define PC_API __attribute__((visibility("default")))
+#else
+#define PC_API
+#endif
+
 typedef int pc_status;
 
 enum {
@@ -83,7 +89,7 @@ enum {
  * Errors: PC_EINVAL, PC_EALIGN (pointer not 16-byte aligned, k % 8 != 0),
  *         PC_EHIP.
  */
-pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t k,
+PC_API pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t k,
                     const int32_t* order, void* stream);
 
 /*
@@ -101,7 +107,7 @@ pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t 
  *          must never read as ready).
  * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
  */
-pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32_t seq, void* stream);
+PC_API pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32_t seq, void* stream);
 
 /*
  * pc_consume_ll -- validate N ranks' LL lines and fold the ready ones.
@@ -120,7 +126,7 @@ pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32_t seq,
  *   out, ready_bitmap and the lines must not overlap one another.
  * Errors: PC_EINVAL, PC_EALIGN (pointer alignment, k % 128 != 0), PC_EHIP.
  */
-pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* out, size_t k,
+PC_API pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* out, size_t k,
                         uint32_t seq, uint64_t* ready_bitmap, void* stream);
 
 /*
@@ -141,7 +147,7 @@ pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* out, size
  * Two kernels are enqueued on `stream`, the copy-out after the slice reduce.
  * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
  */
-pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
+PC_API pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
                      void* stream);
 
 /*
@@ -165,15 +171,15 @@ pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs
  *   out, ready_bitmap and the shards must not overlap one another.
  * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
  */
-pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
+PC_API pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
                             size_t shard_bytes, uint64_t seq, uint64_t* ready_bitmap,
                             void* stream);
 
 /* Static text for a status code (never NULL). */
-const char* pc_strerror(pc_status status);
+PC_API const char* pc_strerror(pc_status status);
 
 /* PC_ABI_VERSION of the loaded library. */
-int pc_abi_version(void);
+PC_API int pc_abi_version(void);
 
 #ifdef __cplusplus
 }

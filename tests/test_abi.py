@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports what include/pc.h declares, and rejects
+bad arguments before launching anything (no GPU needed: the addresses used
+here are never dereferenced, because validation fails or k == 0)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pc.h")
+
+from collective_datapath_amd import binding as B  # noqa: E402
+
+A = 0x7F0000000000        # 16-byte aligned fake device addresses, never touched
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^PC_API\s+[\w\s\*]+?\b(pc_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert getattr(B.library(), name) is not None
+    # No other C entry point of ours is exported (host helpers are hidden;
+    # HIP keeps kernel handle symbols visible, which are C++-mangled).
+    ours = {s for s in syms if s.startswith("pc_")}
+    assert ours == set(declared_functions())
+
+
+def test_version_and_strerror():
+    assert B.pc_abi_version() == 1
+    assert B.pc_strerror(B.PC_OK) == "success"
+    for st in (B.PC_EINVAL, B.PC_EALIGN, B.PC_EUNSUPPORTED, B.PC_EHIP, 12345):
+        assert isinstance(B.pc_strerror(st), str) and B.pc_strerror(st)
+
+
+def ptrs(n, stride=64 * MB, base=A):
+    return [base + r * stride for r in range(n)]
+
+
+OUT = A + 1024 * MB
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(inputs=ptrs(0), out=OUT, k=8), B.PC_EINVAL),
+    (dict(inputs=ptrs(9), out=OUT, k=8), B.PC_EINVAL),
+    (dict(inputs=ptrs(2) + [0], out=OUT, k=8), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), out=0, k=8), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), out=OUT, k=12), B.PC_EALIGN),
+    (dict(inputs=[A, A + 8], out=OUT, k=8), B.PC_EALIGN),
+    (dict(inputs=ptrs(2), out=OUT + 2, k=8), B.PC_EALIGN),
+    (dict(inputs=ptrs(3), out=OUT, k=8, order=[0, 0, 1]), B.PC_EINVAL),
+    (dict(inputs=ptrs(3), out=OUT, k=8, order=[0, 1, 3]), B.PC_EINVAL),
+    (dict(inputs=ptrs(3), out=OUT, k=8, order=[-1, 0, 1]), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), out=A + 16, k=64), B.PC_EINVAL),          # partial overlap
+    (dict(inputs=ptrs(2), out=OUT, k=(1 << 34) + 8), B.PC_EINVAL),   # above the maximum
+    (dict(inputs=ptrs(2), out=OUT, k=0), B.PC_OK),                   # empty: no-op
+    (dict(inputs=[0, 0], out=0, k=0), B.PC_OK),                      # empty tensors
+])
+def test_reduce_validation(args, want):
+    assert B.pc_reduce(stream=0, check=False, **args) == want
+
+
+def test_reduce_binding_checks_order_length():
+    with pytest.raises(ValueError):
+        B.pc_reduce(ptrs(3), OUT, 8, order=[0, 1], stream=0)
+
+
+def test_error_raises_with_status():
+    with pytest.raises(B.PCError) as e:
+        B.pc_reduce(ptrs(9), OUT, 8, stream=0)
+    assert e.value.status == B.PC_EINVAL
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(src=A, dst=OUT, k=8, seq=0), B.PC_EINVAL),
+    (dict(src=A, dst=OUT, k=12, seq=1), B.PC_EALIGN),
+    (dict(src=A + 8, dst=OUT, k=8, seq=1), B.PC_EALIGN),
+    (dict(src=0, dst=OUT, k=8, seq=1), B.PC_EINVAL),
+    (dict(src=A, dst=A + 16, k=64, seq=1), B.PC_EINVAL),
+    (dict(src=A, dst=OUT, k=0, seq=1), B.PC_OK),
+])
+def test_pack_validation(args, want):
+    assert B.pc_pack_ll(stream=0, check=False, **args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(lines=ptrs(2), out=OUT, k=128, seq=0, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(lines=ptrs(9), out=OUT, k=128, seq=1, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(lines=ptrs(2), out=OUT, k=64, seq=1, ready_bitmap=OUT + MB), B.PC_EALIGN),
+    (dict(lines=ptrs(2), out=OUT, k=128, seq=1, ready_bitmap=0), B.PC_EINVAL),
+    (dict(lines=ptrs(2), out=OUT, k=128, seq=1, ready_bitmap=OUT + 8), B.PC_EALIGN),
+    (dict(lines=ptrs(2), out=OUT, k=128, seq=1, ready_bitmap=OUT + 128), B.PC_EINVAL),
+    (dict(lines=ptrs(2), out=A + 64, k=128, seq=1, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(lines=ptrs(2), out=OUT, k=0, seq=1, ready_bitmap=0), B.PC_OK),
+])
+def test_consume_validation(args, want):
+    assert B.pc_consume_ll(stream=0, check=False, **args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(inputs=ptrs(4), outs=ptrs(4, base=OUT), k=8 * 4 + 8), B.PC_EALIGN),
+    (dict(inputs=ptrs(4), outs=ptrs(4, base=OUT, stride=16), k=64 * 4), B.PC_EINVAL),
+    (dict(inputs=ptrs(4), outs=ptrs(4, base=A + 32), k=64 * 4), B.PC_EINVAL),
+    (dict(inputs=ptrs(4), outs=ptrs(4, base=OUT), k=0), B.PC_OK),
+    (dict(inputs=ptrs(9), outs=ptrs(9, base=OUT), k=72), B.PC_EINVAL),
+])
+def test_twoshot_validation(args, want):
+    assert B.pc_twoshot(stream=0, check=False, **args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(shards=ptrs(2), out=OUT, shard_bytes=8192, seq=0, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(shards=ptrs(2), out=OUT, shard_bytes=4096, seq=1, ready_bitmap=OUT + MB), B.PC_EALIGN),
+    (dict(shards=[A, A + 8 + 64 * MB], out=OUT, shard_bytes=8192, seq=1, ready_bitmap=OUT + MB), B.PC_EALIGN),
+    (dict(shards=ptrs(2), out=OUT, shard_bytes=8192, seq=1, ready_bitmap=OUT + 64), B.PC_EINVAL),
+    (dict(shards=ptrs(2), out=A + 4096, shard_bytes=8192, seq=1, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(shards=ptrs(2), out=OUT, shard_bytes=0, seq=1, ready_bitmap=0), B.PC_OK),
+])
+def test_allgather_validation(args, want):
+    assert B.pc_allgather_copy(stream=0, check=False, **args) == want
+
+
+def test_one_hip_runtime_in_process():
+    # The library must share torch's HIP runtime (streams, allocations).
+    assert len(B._hip_runtimes()) == 1

@@ -1,0 +1,343 @@
+"""Parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every comparison is bitwise over whole output and bitmap buffers (0 ULP):
+the fold order is fixed, so each output element has exactly one correct bit
+pattern.  Inputs come from the seeded generators (collective_datapath_amd.synth)
+or from torch's own device RNG, never from the HIP path; expected values come
+from the oracle only.  Outputs are prefilled with 0xFFFF on both sides so
+that "left untouched" is checked too.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from collective_datapath_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from collective_datapath_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def D():
+    import devbuf
+    return devbuf
+
+
+def gpu_reduce(B, D, xs, order=None, out_fill=0xFFFF):
+    k = xs[0].size
+    ins = [D.up(x) for x in xs]
+    out = D.filled(k, out_fill)
+    B.pc_reduce(ins, out, k, order=order)
+    return D.down(out, np.uint16)
+
+
+# ---- reduce -----------------------------------------------------------------
+
+def test_reduce_oneshot_8k(B, D, orc):
+    case = synth.C1_ONESHOT_8K
+    say(case.name)
+    xs = case.inputs()
+    assert np.array_equal(gpu_reduce(B, D, xs), orc.reduce(xs))
+
+
+def test_reduce_oneshot_64m(B, D, orc):
+    case = synth.C4_ONESHOT_64M
+    say(case.name)
+    xs = case.inputs()
+    want = orc.reduce(xs, threads=THREADS)
+    got = gpu_reduce(B, D, xs)
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} mismatches"
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_reduce_every_n_ragged_with_order(B, D, orc, n):
+    # 37 full 256-chunk tiles plus a ragged tail of 5 chunks.
+    k = 8 * (256 * 37 + 5)
+    say("reduce ragged", n, k)
+    xs = [synth.normal_bf16(200 + n, 0, r, k, 3.0) for r in range(n)]
+    order = list(np.random.default_rng(n).permutation(n))
+    assert np.array_equal(gpu_reduce(B, D, xs, order=order), orc.reduce(xs, order=order))
+    assert np.array_equal(gpu_reduce(B, D, xs), orc.reduce(xs))
+
+
+@pytest.mark.parametrize("n,chunks", [
+    (3, 262144 + 1234),           # mid-size shape: 4 MiB per rank and a tail
+    (2, 4718592 + 77),            # streaming shape: 72 MiB per rank and a tail
+    (8, 256 * 2 * 3 + 1),         # one chunk past whole tiles
+    (4, 1),                       # a single chunk
+])
+def test_reduce_regimes_and_tails(B, D, orc, n, chunks):
+    k = 8 * chunks
+    say("reduce regime", n, k)
+    xs = [synth.uniform_bf16(300 + n, 0, r, k) for r in range(n)]
+    assert np.array_equal(gpu_reduce(B, D, xs), orc.reduce(xs, threads=THREADS))
+
+
+def test_reduce_closed_forms(B, D, orc):
+    import json
+    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
+    for case in golden["fold"]["cases"]:
+        xs = [np.full(64, int(v, 16), dtype=np.uint16) for v in case["inputs"]]
+        got = gpu_reduce(B, D, xs, order=case["order"])
+        assert np.all(got == int(case["bf16"], 16)), case
+
+
+@pytest.mark.parametrize("part", range(16))
+def test_reduce_two_ranks_exhaustive(B, D, orc, part):
+    # All 2^32 (x0, x1) bf16 pairs, in 16 parts of 2^28 pairs.
+    say("exhaustive pairs, part", part)
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x1vals = allh[part * 4096:(part + 1) * 4096]
+    x0 = np.tile(allh, x1vals.size)
+    x1 = np.repeat(x1vals, allh.size)
+    want = orc.reduce([x0, x1], threads=THREADS)
+    got = gpu_reduce(B, D, [x0, x1])
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(hex(x0[i]), hex(x1[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+def test_reduce_specials_three_ranks(B, D, orc):
+    sp = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80,
+                   0x7FC0, 0xFFC1, 0x7F81, 0x3F80, 0xBF80, 0x4C00, 0xCC00, 0x3B80, 0x007F],
+                  dtype=np.uint16)
+    a, b, c = np.meshgrid(sp, sp, sp, indexing="ij")
+    xs = [a.reshape(-1), b.reshape(-1), c.reshape(-1)]
+    pad = (-xs[0].size) % 8
+    xs = [np.concatenate([x, np.zeros(pad, np.uint16)]) for x in xs]
+    for order in ([0, 1, 2], [2, 0, 1]):
+        assert np.array_equal(gpu_reduce(B, D, xs, order=order), orc.reduce(xs, order=order))
+
+
+def test_reduce_in_place(B, D, orc):
+    n, k = 4, 8 * 5000
+    xs = [synth.uniform_bf16(400, 0, r, k) for r in range(n)]
+    ins = [D.up(x) for x in xs]
+    B.pc_reduce(ins, ins[2], k)
+    assert np.array_equal(D.down(ins[2], np.uint16), orc.reduce(xs))
+
+
+def test_reduce_same_buffer_as_every_rank(B, D, orc):
+    x = synth.uniform_bf16(401, 0, 0, 4096)
+    t = D.up(x)
+    out = D.filled(4096, 0xFFFF)
+    B.pc_reduce([t] * 8, out, 4096)
+    assert np.array_equal(D.down(out, np.uint16), orc.reduce([x] * 8))
+
+
+def test_reduce_empty_is_noop(B, D):
+    out = D.filled(16, 0x1234)
+    e = torch.empty(0, dtype=torch.int16, device="cuda:0")
+    assert B.pc_reduce([e, e], e, 0) == B.PC_OK
+    assert np.all(D.down(out, np.uint16) == 0x1234)
+
+
+def test_reduce_large_offsets_sampled(B, D, orc):
+    # 4 GiB per rank: byte offsets above 2^32.  Inputs from torch's device RNG;
+    # sampled outputs (first/last tiles, the tail and random points) are
+    # compared with the oracle run on the sampled inputs.
+    n, k = 2, (1 << 31) + 8 * 3
+    say("large offsets", n, k)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(7)
+    ins = [torch.randint(-32768, 32768, (k,), dtype=torch.int32, device="cuda:0",
+                         generator=g).to(torch.int16) for _ in range(n)]
+    out = torch.empty(k, dtype=torch.int16, device="cuda:0")
+    B.pc_reduce(ins, out, k)
+    idx = np.concatenate([np.arange(0, 8192), np.arange(k - 8192, k),
+                          np.random.default_rng(3).integers(0, k, 1 << 16)])
+    it = torch.from_numpy(idx).to("cuda:0")
+    xs = [D.down(t[it], np.uint16) for t in ins]
+    got = D.down(out[it], np.uint16)
+    assert np.array_equal(got, orc.reduce(xs))
+    del ins, out
+    torch.cuda.empty_cache()
+
+
+# ---- LL pack / consume ---------------------------------------------------------
+
+def gpu_pack(B, D, x, seq):
+    src = D.up(x)
+    dst = torch.empty(x.size // 2, dtype=torch.int64, device="cuda:0")
+    B.pc_pack_ll(src, dst, x.size, seq)
+    return dst
+
+
+def stage_gpu(B, D, case):
+    """Stale lines keep the previous call's seq and payload (device side)."""
+    staged = []
+    for x, s, m in zip(case.payloads(), case.stale_payloads(), case.stale_masks()):
+        cur = gpu_pack(B, D, x, case.seq)
+        old = gpu_pack(B, D, s, case.stale_seq)
+        staged.append(torch.where(torch.from_numpy(m).to("cuda:0"), old, cur))
+    return staged
+
+
+def stage_oracle(orc, case):
+    return [np.where(m, orc.pack_ll(s, case.stale_seq), orc.pack_ll(x, case.seq))
+            for x, s, m in zip(case.payloads(), case.stale_payloads(), case.stale_masks())]
+
+
+def test_pack_ll_bits(B, D, orc):
+    case = synth.C2_LL_128K
+    for x in case.payloads()[:2]:
+        assert np.array_equal(D.down(gpu_pack(B, D, x, 7), np.uint64), orc.pack_ll(x, 7))
+    x = synth.uniform_bf16(500, 0, 0, 8 * (512 * 3 + 7))
+    assert np.array_equal(D.down(gpu_pack(B, D, x, 0xDEADBEEF), np.uint64),
+                          orc.pack_ll(x, 0xDEADBEEF))
+
+
+def gpu_consume(B, D, lines_dev, k, seq, out_fill=0xFFFF):
+    out = D.filled(k, out_fill)
+    bm = torch.full((k // 128,), -1, dtype=torch.int64, device="cuda:0")  # must be overwritten
+    B.pc_consume_ll(lines_dev, out, k, seq, bm)
+    return D.down(out, np.uint16), D.down(bm, np.uint64)
+
+
+def test_consume_ll_128k_stale(B, D, orc):
+    case = synth.C2_LL_128K
+    say(case.name)
+    staged_dev = stage_gpu(B, D, case)
+    staged = stage_oracle(orc, case)
+    for a, b in zip(staged_dev, staged):
+        assert np.array_equal(D.down(a, np.uint64), b)
+    want_out, want_bm = orc.consume_ll(staged, case.k, case.seq)
+    got_out, got_bm = gpu_consume(B, D, staged_dev, case.k, case.seq)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+    ready = int(np.unpackbits(got_bm.view(np.uint8)).sum())
+    assert 0.6 * case.lines < ready < 0.72 * case.lines
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (2, 128 * 3), (3, 128 * 37), (8, 128 * 1001), (5, 1 << 20)])
+def test_consume_ll_shapes(B, D, orc, n, k):
+    case = synth.LLCase("shape", 600 + n, n, k, stale_frac=0.03)
+    staged = stage_oracle(orc, case)
+    want_out, want_bm = orc.consume_ll(staged, k, case.seq)
+    got_out, got_bm = gpu_consume(B, D, [D.up(s) for s in staged], k, case.seq)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+
+
+def test_consume_ll_one_rank_identity_all_patterns(B, D, orc):
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    lines = gpu_pack(B, D, allh, 9)
+    got_out, got_bm = gpu_consume(B, D, [lines], allh.size, 9)
+    want_out, want_bm = orc.consume_ll([orc.pack_ll(allh, 9)], allh.size, 9)
+    assert np.array_equal(got_out, want_out)
+    assert np.array_equal(got_bm, want_bm)
+
+
+def test_consume_ll_wrong_seq_and_late_arrival(B, D, orc):
+    case = synth.LLCase("late", 700, 8, 8192)
+    staged = [D.up(s) for s in stage_oracle(orc, case)]
+    out, bm = gpu_consume(B, D, staged, case.k, 8)             # nothing carries seq 8
+    assert np.all(bm == 0) and np.all(out == 0xFFFF)
+    # First consume sees the partial arrival, second after the late lines land.
+    out_t = D.filled(case.k, 0xFFFF)
+    bm_t = torch.empty(case.k // 128, dtype=torch.int64, device="cuda:0")
+    B.pc_consume_ll(staged, out_t, case.k, case.seq, bm_t)
+    landed = [gpu_pack(B, D, x, case.seq) for x in case.payloads()]
+    B.pc_consume_ll(landed, out_t, case.k, case.seq, bm_t)
+    assert np.all(D.down(bm_t, np.uint64) == np.uint64(0xFFFFFFFFFFFFFFFF))
+    assert np.array_equal(D.down(out_t, np.uint16), orc.reduce(case.payloads()))
+
+
+# ---- twoshot -------------------------------------------------------------------
+
+def gpu_twoshot(B, D, xs):
+    k = xs[0].size
+    ins = [D.up(x) for x in xs]
+    outs = [D.filled(k, 0xFFFF) for _ in xs]
+    B.pc_twoshot(ins, outs, k)
+    return [D.down(o, np.uint16) for o in outs]
+
+
+def test_twoshot_1m(B, D, orc):
+    case = synth.C3_TWOSHOT_1M
+    say(case.name)
+    xs = case.inputs()
+    want = orc.twoshot(xs)
+    got = gpu_twoshot(B, D, xs)
+    oneshot = gpu_reduce(B, D, xs)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+        assert np.array_equal(g, oneshot)
+
+
+@pytest.mark.parametrize("n,slice_chunks", [(2, 1), (3, 257), (5, 256 * 4 + 3), (8, 300000 + 5), (1, 100)])
+def test_twoshot_shapes(B, D, orc, n, slice_chunks):
+    k = 8 * n * slice_chunks
+    say("twoshot", n, k)
+    xs = [synth.normal_bf16(800 + n, 0, r, k) for r in range(n)]
+    want = orc.reduce(xs, threads=THREADS)
+    for g in gpu_twoshot(B, D, xs):
+        assert np.array_equal(g, want)
+
+
+def test_twoshot_in_place(B, D, orc):
+    n, k = 4, 8 * 4 * 999
+    xs = [synth.normal_bf16(900, 0, r, k) for r in range(n)]
+    ins = [D.up(x) for x in xs]
+    B.pc_twoshot(ins, ins, k)
+    want = orc.reduce(xs)
+    for t in ins:
+        assert np.array_equal(D.down(t, np.uint16), want)
+
+
+# ---- all-gather copy -------------------------------------------------------------
+
+def gpu_allgather(B, D, recs, n, shard_bytes, seq):
+    shards = [D.up(r) for r in recs]
+    out = D.filled(n * shard_bytes // 2, 0xFFFF)
+    bm = torch.full((n * shard_bytes // 128 // 64,), -1, dtype=torch.int64, device="cuda:0")
+    B.pc_allgather_copy(shards, out, shard_bytes, seq, bm)
+    return D.down(out, np.uint16), D.down(bm, np.uint64)
+
+
+def test_allgather_2m_stale(B, D, orc):
+    case = synth.C5_ALLGATHER_2M
+    say(case.name)
+    recs, _ = case.records()
+    want_out, want_bm = orc.allgather_copy(recs, case.shard_bytes, case.seq)
+    got_out, got_bm = gpu_allgather(B, D, recs, case.n, case.shard_bytes, case.seq)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+    assert int(np.unpackbits(got_bm.view(np.uint8)).sum()) == 131072 - 8 * 1638
+
+
+@pytest.mark.parametrize("n,shard_bytes,frac", [(1, 8192, 0.5), (3, 8192 * 3, 0.1),
+                                                 (8, 8192 * 17, 0.0), (2, 8192 * 5, 1.0)])
+def test_allgather_shapes(B, D, orc, n, shard_bytes, frac):
+    case = synth.GatherCase("shape", 1000 + n, n, shard_bytes, stale_frac=frac)
+    recs, _ = case.records()
+    want_out, want_bm = orc.allgather_copy(recs, shard_bytes, case.seq)
+    got_out, got_bm = gpu_allgather(B, D, recs, n, shard_bytes, case.seq)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+
+
+def test_allgather_header_compared_as_u64(B, D, orc):
+    # A header whose low 32 bits match seq but high bits differ is stale.
+    case = synth.GatherCase("hi bits", 1100, 2, 8192, stale_frac=0.0)
+    recs, _ = case.records()
+    recs[1] = recs[1].copy()
+    recs[1].view(np.uint64)[17 * 5] = np.uint64((1 << 32) | case.seq)
+    want_out, want_bm = orc.allgather_copy(recs, 8192, case.seq)
+    got_out, got_bm = gpu_allgather(B, D, recs, 2, 8192, case.seq)
+    assert np.array_equal(got_bm, want_bm) and np.array_equal(got_out, want_out)
+    assert int(np.unpackbits(got_bm.view(np.uint8)).sum()) == 127
