@@ -34,6 +34,15 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the headline kernel from two rocprofv3 counter runs
+# (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
+# copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
+# values.  Reported only while the kernel sources hash to what was profiled.
+TRAFFIC = {"bytes": 604039883,
+           "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
+                       "collective_datapath_amd/csrc/pc_device.hpp"),
+           "sha256": "4dd7d21a447dcaca345e7a3d995f65df2d698e53006c34db6985560d9c5216f7"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -112,8 +121,11 @@ class Dev:
 
 
 def timing(d, fn, steps, warmup):
+    """graph_us: per-call time inside a HIP graph (device-side latency);
+    eager_us: back-to-back eager calls from Python, which for small payloads
+    measures the host launch path rather than the GPU."""
     ms = d.events_ms(fn, steps, warmup)
-    return {"kernel_us": round(ms * 1000.0, 3), "graph_us": round(d.graph_us(fn), 3)}
+    return {"graph_us": round(d.graph_us(fn), 3), "eager_us": round(ms * 1000.0, 3)}
 
 
 def gbs(nbytes, us):
@@ -135,8 +147,9 @@ def run_headline(d, B, synth, args, out):
     g_us = d.graph_us(fn, calls=16, replays=4)
     nbytes = case.bytes_moved()
     ach = gbs(nbytes, ms * 1000.0)
-    out["headline"] = {"workload": case.name, "bytes_per_call": nbytes, "kernel_us": round(ms * 1e3, 3),
-                       "graph_us": round(g_us, 3), "gbs": round(ach, 1)}
+    out["headline"] = {"workload": case.name, "bytes_per_call": nbytes,
+                       "event_us_per_launch": round(ms * 1e3, 3), "graph_us": round(g_us, 3),
+                       "gbs": round(ach, 1)}
     got = d.down(res, np.uint16)
     if not args.no_parity or not args.no_cpu_baseline:
         import oracle
@@ -166,6 +179,19 @@ def run_headline(d, B, synth, args, out):
     return ms, ach
 
 
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    return TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sha256"] else None
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -184,7 +210,7 @@ def run_c1(d, B, synth, oracle, args, out):
     res = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
     t = timing(d, lambda: B.pc_reduce(ins, res, case.k), 2000, 100)
     t.update(workload=case.name, bytes_per_call=case.bytes_moved(),
-             gbs_cache_resident=round(gbs(case.bytes_moved(), t["kernel_us"]), 1))
+             gbs_cache_resident=round(gbs(case.bytes_moved(), t["graph_us"]), 1))
     out["configs"]["oneshot_8k"] = t
     if oracle is not None:
         out["parity"]["oneshot_8k"] = bool(np.array_equal(d.down(res, np.uint16), oracle.reduce(xs)))
@@ -210,9 +236,9 @@ def run_c2(d, B, synth, oracle, args, out):
     ready = int(np.unpackbits(bits.view(np.uint8)).sum())
     cbytes = case.n * case.lines * 8 + 4 * ready + case.lines // 8
     tc.update(workload=case.name, ready_lines=ready, bytes_per_call=cbytes,
-              gbs_cache_resident=round(gbs(cbytes, tc["kernel_us"]), 1))
+              gbs_cache_resident=round(gbs(cbytes, tc["graph_us"]), 1))
     tp.update(workload="LL pack of one rank, 128 KiB -> 256 KiB", bytes_per_call=6 * case.k,
-              gbs_cache_resident=round(gbs(6 * case.k, tp["kernel_us"]), 1))
+              gbs_cache_resident=round(gbs(6 * case.k, tp["graph_us"]), 1))
     out["configs"]["ll_consume_128k"] = tc
     out["configs"]["ll_pack_128k"] = tp
     if oracle is not None:
@@ -236,7 +262,7 @@ def run_c3(d, B, synth, oracle, args, out):
     t = timing(d, lambda: B.pc_twoshot(ins, outs, case.k), 1000, 50)
     nbytes = 2 * case.k * (2 * case.n + 1)
     t.update(workload=case.name, bytes_per_call=nbytes,
-             gbs_cache_resident=round(gbs(nbytes, t["kernel_us"]), 1))
+             gbs_cache_resident=round(gbs(nbytes, t["graph_us"]), 1))
     out["configs"]["twoshot_1m"] = t
     if oracle is not None:
         want = oracle.twoshot(xs)
@@ -257,7 +283,7 @@ def run_c5(d, B, synth, oracle, args, out):
     ready = int(sum((~m).sum() for m in masks))
     nbytes = case.n * case.blocks * 136 + ready * 128 + case.n * case.blocks // 8
     t.update(workload=case.name, ready_blocks=ready, bytes_per_call=nbytes,
-             gbs_cache_resident=round(gbs(nbytes, t["kernel_us"]), 1))
+             gbs_cache_resident=round(gbs(nbytes, t["graph_us"]), 1))
     out["configs"]["allgather_2m"] = t
     if oracle is not None:
         wo, wb = oracle.allgather_copy(recs, case.shard_bytes, case.seq)
@@ -282,7 +308,7 @@ def run_sweep(d, B, synth, oracle, args, out):
                 moved = (2 * n + 1) * nbytes
             t = timing(d, fn, 500, 50)
             row = {"call": kind, "n": n, "bytes_per_rank": nbytes, **t,
-                   "gbs_cache_resident": round(gbs(moved, t["kernel_us"]), 1)}
+                   "gbs_cache_resident": round(gbs(moved, t["graph_us"]), 1)}
             if oracle is not None:
                 want = oracle.reduce(xs)
                 got = d.down(res if kind == "reduce" else outs[n - 1], np.uint16)
@@ -303,7 +329,7 @@ def run_copy(d, out, steps):
     a = torch.empty(128 << 20, dtype=torch.int16, device=d.dev).fill_(1)
     b = torch.empty_like(a)
     ms = d.events_ms(lambda: b.copy_(a), steps, 5)
-    out["copy_256m"] = {"kernel_us": round(ms * 1e3, 3), "bytes_per_call": 2 * (256 << 20),
+    out["copy_256m"] = {"event_us": round(ms * 1e3, 3), "bytes_per_call": 2 * (256 << 20),
                         "gbs": round(gbs(2 * (256 << 20), ms * 1e3), 1)}
 
 
@@ -352,7 +378,8 @@ def main():
                        "n": 8, "k": 4096 * 8192, "bytes_per_call": 9 * 2 * 4096 * 8192}}
     if ach:
         line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic(),
                             "kernel": "pcdp::k_reduce<8, 4, true, false>"}
     if "cpu_baseline" in out:
         line["cpu_baseline"] = out.pop("cpu_baseline")
