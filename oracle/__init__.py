@@ -21,9 +21,12 @@ _LIB: Optional[ctypes.CDLL] = None
 def lib() -> ctypes.CDLL:
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
+        # PC_ORACLE_LIB points the pins at a deliberately broken build of the
+        # oracle (tests/test_oracle_mutants.py); normal runs never set it.
+        path = os.environ.get("PC_ORACLE_LIB", _build.LIB)
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.orc_fpenv_ok.restype = I
         L.orc_widen.argtypes = [ctypes.c_uint16]

@@ -328,6 +328,17 @@ def test_allgather_one_hot_stale_pins_position(orc):
     assert np.array_equal(out, want)
 
 
+def test_allgather_header_is_compared_as_u64(orc):
+    case = synth.GatherCase("hi bits", 97, 2, 8192, stale_frac=0.0)
+    recs, _ = case.records()
+    recs[1] = recs[1].copy()
+    recs[1].view(np.uint64)[17 * 5] = np.uint64((1 << 32) | case.seq)
+    out, bm = orc.allgather_copy(recs, case.shard_bytes, case.seq)
+    want_bm = np.full(2, 0xFFFFFFFFFFFFFFFF, dtype=np.uint64)
+    want_bm[1] &= ~np.uint64(1 << 5)
+    assert np.array_equal(bm, want_bm)
+
+
 def test_allgather_stale_workload(orc):
     case = synth.C5_ALLGATHER_2M
     recs, masks = case.records()
