@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604039883,
+TRAFFIC = {"bytes": 604054110,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "4dd7d21a447dcaca345e7a3d995f65df2d698e53006c34db6985560d9c5216f7"}
+           "sha256": "4581b63730ac5c9047e5062ca963de628dcb9d3313b62aa4362c3eab8e65ada6"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -380,7 +380,7 @@ def main():
         line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(),
-                            "kernel": "pcdp::k_reduce<8, 4, true, false>"}
+                            "kernel": "pcdp::k_reduce_persistent<8, false>"}
     if "cpu_baseline" in out:
         line["cpu_baseline"] = out.pop("cpu_baseline")
     line.update(out)

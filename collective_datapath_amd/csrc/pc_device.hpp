@@ -20,6 +20,7 @@ namespace pcdp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxRanks = 8;
 constexpr int kWave = 64;
@@ -43,6 +44,21 @@ template <bool kStream>
 __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
     if constexpr (kStream) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+// Store through a buffer resource with device-scope cache policy (sc1) and no
+// non-temporal hint.  For the bandwidth regime this is measurably better for
+// HBM than non-temporal stores when writes are mixed with a large read stream.
+// The resource covers [base, base + bytes); `byte_off` is within it.
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9
+constexpr int kPolicyDeviceScope = 0x10;  // sc1
+
+__device__ __forceinline__ void store16_device_scope(u32x4* base, uint32_t bytes, uint32_t byte_off,
+                                                     u32x4 v) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rs, byte_off, 0,
+                                           kPolicyDeviceScope);
 }
 
 // ---- bf16 <-> fp32 ----------------------------------------------------------

@@ -63,6 +63,63 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
     }
 }
 
+// ---- bandwidth regime: persistent slice reduce ------------------------------------
+// For working sets far beyond the last-level cache.  The grid is sized by the
+// host to whole rounds of at most two workgroups per CU, and workgroup w takes
+// tiles w, w + grid, w + 2*grid, ...  Each tile is 16 KiB per rank.  Within a
+// tile every lane issues all 4*N non-temporal loads, folds its 4 chunks, and
+// the workgroup then issues its stores together (after a barrier) with
+// device-scope stores.  Keeping each workgroup's writes in one burst after
+// its reads, rather than interleaved with them, measurably raises HBM
+// efficiency for this 8:1 read/write mix; so do the two-per-CU persistent
+// grid and the store policy (see the design notes for the measurements).
+// Grid tile g covers slice g / tiles_per_slice.
+template <int N, bool kSliced>
+__global__ __launch_bounds__(kBlock) void k_reduce_persistent(Ptrs<const u32x4*> src,
+                                                                Ptrs<u32x4*> dst, uint32_t nslice,
+                                                                uint32_t tiles_per_slice,
+                                                                uint32_t ntiles) {
+    constexpr int U = 4;
+    constexpr uint32_t kTile = kBlock * U;
+    const uint32_t t = threadIdx.x;
+    for (uint32_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
+        const uint32_t s = kSliced ? g / tiles_per_slice : 0u;
+        const uint32_t tile0 = (g - s * tiles_per_slice) * kTile;
+        const size_t first = (size_t)s * nslice + tile0;
+        const uint32_t left = nslice - tile0;
+        u32x4* out = dst.p[s] + first;
+        const u32x4* in[N];
+#pragma unroll
+        for (int r = 0; r < N; ++r) in[r] = src.p[r] + first;
+        if (left >= kTile) {
+            u32x4 v[U][N];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < N; ++r) v[u][r] = load16<true>(in[r] + u * kBlock + t);
+            u32x4 o[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) o[u] = fold_chunk<N>(v[u]);
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                store16_device_scope(out, kTile * 16u, (u * kBlock + t) * 16u, o[u]);
+        } else {
+            // Ragged last tile of a slice (uniform branch for the workgroup).
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t c = u * kBlock + t;
+                if (c < left) {
+                    u32x4 v[N];
+#pragma unroll
+                    for (int r = 0; r < N; ++r) v[r] = load16<true>(in[r] + c);
+                    store16_device_scope(out, left * 16u, c * 16u, fold_chunk<N>(v));
+                }
+            }
+        }
+    }
+}
+
 // ---- twoshot copy-out: the owner's slice goes to every other rank's output ----
 // Grid: x = tile within a slice, y = slice s.  Reads outs[s] once per chunk
 // and writes it to the N-1 other outputs.
@@ -97,8 +154,23 @@ __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t 
 // Shapes by payload: small payloads (latency regime, cache resident) take one
 // chunk per lane so the most workgroups start at once; mid payloads take two;
 // payloads whose working set is far beyond the 256 MiB of last-level cache
-// stream with non-temporal hints and four chunks per lane per rank.
+// use the persistent kernel above.
 enum class Regime { kSmall, kMid, kStream };
+
+// Compute units of the current device, looked up once per device.
+static uint32_t device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int cus = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        __atomic_store_n(&cached[dev], cus, __ATOMIC_RELAXED);
+    }
+    return (uint32_t)cus;
+}
 
 static Regime pick_regime(size_t nchunks_per_rank, int n) {
     const size_t per_rank = nchunks_per_rank * 16;
@@ -119,10 +191,27 @@ static hipError_t go_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t n
 }
 
 template <int N, bool kSliced>
+static hipError_t go_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                                       uint32_t slices, hipStream_t stream) {
+    constexpr uint32_t kTile = kBlock * 4;
+    uint32_t tiles_per_slice = (nslice + kTile - 1) / kTile;
+    uint32_t ntiles = tiles_per_slice * slices;
+    // Whole rounds of at most two workgroups per CU, then as few workgroups
+    // as give that many rounds, so every workgroup does the same number of
+    // tiles (to within one).
+    const uint32_t slots = 2 * device_cus();
+    const uint32_t rounds = (ntiles + slots - 1) / slots;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    void* args[] = {&src, &dst, &nslice, &tiles_per_slice, &ntiles};
+    return hipLaunchKernel((const void*)&k_reduce_persistent<N, kSliced>, dim3(grid), dim3(kBlock),
+                           args, 0, stream);
+}
+
+template <int N, bool kSliced>
 static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                    uint32_t nslice, uint32_t slices, hipStream_t stream) {
     switch (rg) {
-        case Regime::kStream: return go_reduce<N, 4, true, kSliced>(src, dst, nslice, slices, stream);
+        case Regime::kStream: return go_reduce_persistent<N, kSliced>(src, dst, nslice, slices, stream);
         case Regime::kMid: return go_reduce<N, 2, false, kSliced>(src, dst, nslice, slices, stream);
         default: return go_reduce<N, 1, false, kSliced>(src, dst, nslice, slices, stream);
     }

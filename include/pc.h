@@ -112,7 +112,7 @@ PC_API pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32
 /*
  * pc_consume_ll -- validate N ranks' LL lines and fold the ready ones.
  * Source: flash-comm, Section 4.3 (one-hop: poll the source slots, reduce only
- * once all contributions are available, fold by source rank in rank order),
+ * once every source has arrived, fold by source rank in rank order),
  * Section 3.1 (accept a unit only when its sequence number matches the
  * current call), Section 3.3 (rank order 0..N-1).
  *   lines  : host array of n device pointers, each to k/2 uint64 lines.

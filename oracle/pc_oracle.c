@@ -10,7 +10,8 @@
  *  - "Purlin: Separating Orchestration from the Datapath of Collectives",
  *    Section 3.3 (The Atom's Unified Pipeline), paragraph "Deterministic
  *    reduction within the pipeline", Equation (2): one accumulator per output
- *    element, contributions added in ascending rank order starting from zero;
+ *    element, contributions added rank by rank in ascending order, the sum
+ *    beginning at zero;
  *    each input widened from its type to FP32, accumulated in FP32, and the sum
  *    converted back to the element type only after it is complete.
  *  - "flash-comm: Self-Synchronizing Collective Communication for LLM
