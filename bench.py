@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604054110,
+TRAFFIC = {"bytes": 604016195,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "4581b63730ac5c9047e5062ca963de628dcb9d3313b62aa4362c3eab8e65ada6"}
+           "sha256": "7290097cc08dbb5b6606992b7aabecf27954aaec3c89442d65892b2596b1ad94"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -258,19 +258,23 @@ def run_c3(d, B, synth, oracle, args, out):
     case = synth.C3_TWOSHOT_1M
     xs = case.inputs()
     ins = [d.up(x) for x in xs]
-    outs = [d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev) for _ in xs]
-    t = timing(d, lambda: B.pc_twoshot(ins, outs, case.k), 1000, 50)
-    nbytes = 2 * case.k * (2 * case.n + 1)
-    t.update(workload=case.name, bytes_per_call=nbytes,
-             gbs_cache_resident=round(gbs(nbytes, t["graph_us"]), 1))
-    out["configs"]["twoshot_1m"] = t
+    want = oracle.twoshot(xs) if oracle is not None else None
+    onev = None
     if oracle is not None:
-        want = oracle.twoshot(xs)
         one = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
         B.pc_reduce(ins, one, case.k)
         onev = d.down(one, np.uint16)
-        out["parity"]["twoshot_1m"] = bool(all(np.array_equal(d.down(o, np.uint16), w) and
-                                               np.array_equal(w, onev) for o, w in zip(outs, want)))
+    # Two launches (slice reduce, then copy-out) and the single-launch form.
+    for name, fn, nbytes in (("twoshot_1m", B.pc_twoshot, 2 * case.k * (2 * case.n + 1)),
+                             ("twoshot_fused_1m", B.pc_twoshot_fused, 2 * case.k * 2 * case.n)):
+        outs = [d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev) for _ in xs]
+        t = timing(d, lambda: fn(ins, outs, case.k), 1000, 50)
+        t.update(workload=case.name, bytes_per_call=nbytes,
+                 gbs_cache_resident=round(gbs(nbytes, t["graph_us"]), 1))
+        out["configs"][name] = t
+        if oracle is not None:
+            out["parity"][name] = bool(all(np.array_equal(d.down(o, np.uint16), w) and
+                                           np.array_equal(w, onev) for o, w in zip(outs, want)))
 
 
 def run_c5(d, B, synth, oracle, args, out):
@@ -295,17 +299,21 @@ def run_sweep(d, B, synth, oracle, args, out):
     rows = []
     for nbytes in synth.SWEEP_BYTES:
         k = nbytes // 2
-        for kind, n in (("reduce", 4), ("reduce", 8), ("twoshot", 8)):
+        for kind, n in (("reduce", 4), ("reduce", 8), ("twoshot", 8), ("twoshot_fused", 8)):
             xs = [synth.uniform_bf16(20, 0, r, k) for r in range(n)]
             ins = [d.up(x) for x in xs]
             if kind == "reduce":
                 res = d.torch.empty(k, dtype=d.torch.int16, device=d.dev)
                 fn = lambda: B.pc_reduce(ins, res, k)  # noqa: E731
                 moved = (n + 1) * nbytes
-            else:
+            elif kind == "twoshot":
                 outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
                 fn = lambda: B.pc_twoshot(ins, outs, k)  # noqa: E731
                 moved = (2 * n + 1) * nbytes
+            else:
+                outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
+                fn = lambda: B.pc_twoshot_fused(ins, outs, k)  # noqa: E731
+                moved = 2 * n * nbytes
             t = timing(d, fn, 500, 50)
             row = {"call": kind, "n": n, "bytes_per_rank": nbytes, **t,
                    "gbs_cache_resident": round(gbs(moved, t["graph_us"]), 1)}
@@ -380,7 +388,7 @@ def main():
         line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(),
-                            "kernel": "pcdp::k_reduce_persistent<8, false>"}
+                            "kernel": "pcdp::k_reduce_persistent<8, (pcdp::Out)0>"}
     if "cpu_baseline" in out:
         line["cpu_baseline"] = out.pop("cpu_baseline")
     line.update(out)

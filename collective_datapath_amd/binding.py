@@ -21,8 +21,8 @@ PC_BLOCK_PAYLOAD_BYTES = 128
 PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
-EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_allgather_copy",
-           "pc_strerror", "pc_abi_version")
+EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
+           "pc_allgather_copy", "pc_strerror", "pc_abi_version")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -58,8 +58,10 @@ _lib.pc_reduce.argtypes = [_P, _I, _P, _S, _P, _P]
 _lib.pc_pack_ll.argtypes = [_P, _P, _S, ctypes.c_uint32, _P]
 _lib.pc_consume_ll.argtypes = [_P, _I, _P, _S, ctypes.c_uint32, _P, _P]
 _lib.pc_twoshot.argtypes = [_P, _I, _P, _S, _P]
+_lib.pc_twoshot_fused.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
-for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_allgather_copy"):
+for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
+           "pc_allgather_copy"):
     getattr(_lib, _f).restype = _I
 _lib.pc_strerror.argtypes = [_I]
 _lib.pc_strerror.restype = ctypes.c_char_p
@@ -142,6 +144,14 @@ def pc_twoshot(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=
         raise ValueError("pc_twoshot needs one output per input")
     st = _lib.pc_twoshot(_addrs(inputs), len(inputs), _addrs(outs), k, _stream(stream))
     return _call("pc_twoshot", st, check)
+
+
+def pc_twoshot_fused(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=None,
+                     check: bool = True) -> int:
+    if len(outs) != len(inputs):
+        raise ValueError("pc_twoshot_fused needs one output per input")
+    st = _lib.pc_twoshot_fused(_addrs(inputs), len(inputs), _addrs(outs), k, _stream(stream))
+    return _call("pc_twoshot_fused", st, check)
 
 
 def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, seq: int,

@@ -101,11 +101,17 @@ pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* out, size
                                             static_cast<hipStream_t>(stream)));
 }
 
-pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
-                     void* stream) {
+// Shared admission of the two twoshot entry points.  On PC_OK with k > 0 the
+// pointers are copied to src/dst; *empty is set for the k == 0 no-op.
+static pc_status check_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs,
+                               size_t k, const void** src, void** dst, bool* empty) {
+    *empty = false;
     if (!valid_n(n) || !inputs || !outs || k > PC_MAX_ELEMS) return PC_EINVAL;
     if (k % (8 * (size_t)n)) return PC_EALIGN;
-    if (k == 0) return PC_OK;
+    if (k == 0) {
+        *empty = true;
+        return PC_OK;
+    }
     if (pc_status st = check_ptrs(inputs, n)) return st;
     if (pc_status st = check_ptrs(outs, n)) return st;
     const size_t bytes = k * sizeof(uint16_t);
@@ -115,14 +121,33 @@ pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs
         for (int r = 0; r < n; ++r)
             if (inputs[r] != outs[a] && overlaps(inputs[r], bytes, outs[a], bytes)) return PC_EINVAL;
     }
-    const void* src[PC_MAX_RANKS];
-    void* dst[PC_MAX_RANKS];
     for (int r = 0; r < n; ++r) {
         src[r] = inputs[r];
         dst[r] = outs[r];
     }
+    return PC_OK;
+}
+
+pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
+                     void* stream) {
+    const void* src[PC_MAX_RANKS];
+    void* dst[PC_MAX_RANKS];
+    bool empty;
+    if (pc_status st = check_twoshot(inputs, n, outs, k, src, dst, &empty)) return st;
+    if (empty) return PC_OK;
     return from_hip(pcdp::launch_twoshot(src, n, dst, k / 8 / (size_t)n,
                                          static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
+                           void* stream) {
+    const void* src[PC_MAX_RANKS];
+    void* dst[PC_MAX_RANKS];
+    bool empty;
+    if (pc_status st = check_twoshot(inputs, n, outs, k, src, dst, &empty)) return st;
+    if (empty) return PC_OK;
+    return from_hip(pcdp::launch_twoshot_fused(src, n, dst, k / 8 / (size_t)n,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,

@@ -46,17 +46,30 @@ __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
     else *p = v;
 }
 
-// Store through a buffer resource with device-scope cache policy (sc1) and no
-// non-temporal hint.  For the bandwidth regime this is measurably better for
-// HBM than non-temporal stores when writes are mixed with a large read stream.
-// The resource covers [base, base + bytes); `byte_off` is within it.
-constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9
+// Buffer-resource access for the bandwidth regime.  A resource covers one
+// tile, [base, base + bytes), with a scalar base address, so every lane
+// addresses with a 32-bit offset.  The hardware range check makes a ragged
+// last tile branch-free: loads past `bytes` return zero and stores past it
+// are discarded (offsets and `bytes` are multiples of 16, so a 16-byte
+// access is either wholly inside or wholly outside).
+// Loads carry the non-temporal hint; stores use device-scope cache policy
+// (sc1) without it, which GPU measurements showed is markedly better for HBM
+// than non-temporal stores when writes are mixed into a large read stream.
+constexpr int kRsrcWord3 = 0x00020000;    // raw (untyped) buffer access on gfx9
+constexpr int kPolicyNonTemporal = 0x02;  // nt
 constexpr int kPolicyDeviceScope = 0x10;  // sc1
 
-__device__ __forceinline__ void store16_device_scope(u32x4* base, uint32_t bytes, uint32_t byte_off,
-                                                     u32x4 v) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kRsrcWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kPolicyNonTemporal));
+}
+
+__device__ __forceinline__ void store16_tile(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rs, byte_off, 0,
                                            kPolicyDeviceScope);
 }

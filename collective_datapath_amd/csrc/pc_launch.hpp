@@ -22,6 +22,11 @@ hipError_t launch_reduce(const void* const* src, int n, void* out, size_t nchunk
 hipError_t launch_twoshot(const void* const* src, int n, void* const* outs,
                           size_t nchunks_slice, hipStream_t stream);
 
+// Single-launch twoshot: slice s folded once, in rank order, and written by
+// the same workgroup to every outs[r].
+hipError_t launch_twoshot_fused(const void* const* src, int n, void* const* outs,
+                                size_t nchunks_slice, hipStream_t stream);
+
 // LL lines: 16-byte chunks of src -> 4 lines each.
 hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t seq,
                           hipStream_t stream);

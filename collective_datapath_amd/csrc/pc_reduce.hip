@@ -24,19 +24,33 @@ namespace pcdp {
 
 constexpr int kBlock = 256;
 
+// Where a folded chunk goes.  kOne: dst.p[0] (oneshot reduce).  kOwner:
+// dst.p[s], the owner of slice s (twoshot phase 1).  kAll: every dst.p[r]
+// (single-launch twoshot: the owner folds its block once and distributes it).
+enum class Out { kOne, kOwner, kAll };
+
+template <int N, Out kOut, bool kStream>
+__device__ __forceinline__ void put_chunk(const Ptrs<u32x4*>& dst, uint32_t s, size_t at, u32x4 v) {
+    if constexpr (kOut == Out::kAll) {
+#pragma unroll
+        for (int r = 0; r < N; ++r) store16<kStream>(dst.p[r] + at, v);
+    } else {
+        store16<kStream>(dst.p[kOut == Out::kOwner ? s : 0] + at, v);
+    }
+}
+
 // ---- slice reduce (oneshot when there is one slice) ----------------------------
 // Grid: x = tile within a slice, y = slice.  Slice s covers chunks
-// [s*nslice, (s+1)*nslice) of every input and lands in dst.p[kSliced ? s : 0].
-template <int N, int U, bool kStream, bool kSliced>
+// [s*nslice, (s+1)*nslice) of every input; where its folds go is set by kOut.
+template <int N, int U, bool kStream, Out kOut>
 __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                                      uint32_t nslice) {
     constexpr uint32_t kTile = kBlock * U;
-    const uint32_t s = kSliced ? blockIdx.y : 0u;
+    const uint32_t s = kOut == Out::kOne ? 0u : blockIdx.y;
     const uint32_t tile0 = blockIdx.x * kTile;
     const size_t first = (size_t)s * nslice + tile0;
     const uint32_t left = nslice - tile0;
     const uint32_t t = threadIdx.x;
-    u32x4* out = dst.p[s] + first;
     const u32x4* in[N];
 #pragma unroll
     for (int r = 0; r < N; ++r) in[r] = src.p[r] + first;
@@ -48,7 +62,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
 #pragma unroll
             for (int r = 0; r < N; ++r) v[u][r] = load16<kStream>(in[r] + u * kBlock + t);
 #pragma unroll
-        for (int u = 0; u < U; ++u) store16<kStream>(out + u * kBlock + t, fold_chunk<N>(v[u]));
+        for (int u = 0; u < U; ++u)
+            put_chunk<N, kOut, kStream>(dst, s, first + u * kBlock + t, fold_chunk<N>(v[u]));
     } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -57,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
                 u32x4 v[N];
 #pragma unroll
                 for (int r = 0; r < N; ++r) v[r] = load16<kStream>(in[r] + c);
-                store16<kStream>(out + c, fold_chunk<N>(v));
+                put_chunk<N, kOut, kStream>(dst, s, first + c, fold_chunk<N>(v));
             }
         }
     }
@@ -66,15 +81,15 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
 // ---- bandwidth regime: persistent slice reduce ------------------------------------
 // For working sets far beyond the last-level cache.  The grid is sized by the
 // host to whole rounds of at most two workgroups per CU, and workgroup w takes
-// tiles w, w + grid, w + 2*grid, ...  Each tile is 16 KiB per rank.  Within a
-// tile every lane issues all 4*N non-temporal loads, folds its 4 chunks, and
-// the workgroup then issues its stores together (after a barrier) with
-// device-scope stores.  Keeping each workgroup's writes in one burst after
-// its reads, rather than interleaved with them, measurably raises HBM
-// efficiency for this 8:1 read/write mix; so do the two-per-CU persistent
-// grid and the store policy (see the design notes for the measurements).
+// tiles w, w + grid, w + 2*grid, ...  Each tile is 16 KiB per rank, accessed
+// through tile-sized buffer resources (a ragged last tile needs no branch).
+// Every lane issues all 4*N non-temporal loads and folds its 4 chunks; the
+// workgroup then passes a barrier and issues its stores together, as
+// device-scope stores.  Keeping each workgroup's writes in one burst after its
+// reads, the two-per-CU persistent grid, and the store policy each measurably
+// raise HBM efficiency for this 8:1 read/write mix (see the design notes).
 // Grid tile g covers slice g / tiles_per_slice.
-template <int N, bool kSliced>
+template <int N, Out kOut>
 __global__ __launch_bounds__(kBlock) void k_reduce_persistent(Ptrs<const u32x4*> src,
                                                                 Ptrs<u32x4*> dst, uint32_t nslice,
                                                                 uint32_t tiles_per_slice,
@@ -83,39 +98,29 @@ __global__ __launch_bounds__(kBlock) void k_reduce_persistent(Ptrs<const u32x4*>
     constexpr uint32_t kTile = kBlock * U;
     const uint32_t t = threadIdx.x;
     for (uint32_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
-        const uint32_t s = kSliced ? g / tiles_per_slice : 0u;
+        const uint32_t s = kOut == Out::kOne ? 0u : g / tiles_per_slice;
         const uint32_t tile0 = (g - s * tiles_per_slice) * kTile;
         const size_t first = (size_t)s * nslice + tile0;
         const uint32_t left = nslice - tile0;
-        u32x4* out = dst.p[s] + first;
-        const u32x4* in[N];
+        const uint32_t bytes = (left < kTile ? left : kTile) * 16u;
+        u32x4 v[U][N];
 #pragma unroll
-        for (int r = 0; r < N; ++r) in[r] = src.p[r] + first;
-        if (left >= kTile) {
-            u32x4 v[U][N];
+        for (int r = 0; r < N; ++r) {
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, bytes);
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u) v[u][r] = load16_tile(rs, (u * kBlock + t) * 16u);
+        }
+        u32x4 o[U];
 #pragma unroll
-                for (int r = 0; r < N; ++r) v[u][r] = load16<true>(in[r] + u * kBlock + t);
-            u32x4 o[U];
+        for (int u = 0; u < U; ++u) o[u] = fold_chunk<N>(v[u]);
+        __syncthreads();
+        constexpr int kFan = kOut == Out::kAll ? N : 1;
 #pragma unroll
-            for (int u = 0; u < U; ++u) o[u] = fold_chunk<N>(v[u]);
-            __syncthreads();
+        for (int f = 0; f < kFan; ++f) {
+            const int d = kOut == Out::kAll ? f : (kOut == Out::kOwner ? (int)s : 0);
+            const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dst.p[d] + first, bytes);
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                store16_device_scope(out, kTile * 16u, (u * kBlock + t) * 16u, o[u]);
-        } else {
-            // Ragged last tile of a slice (uniform branch for the workgroup).
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t c = u * kBlock + t;
-                if (c < left) {
-                    u32x4 v[N];
-#pragma unroll
-                    for (int r = 0; r < N; ++r) v[r] = load16<true>(in[r] + c);
-                    store16_device_scope(out, left * 16u, c * 16u, fold_chunk<N>(v));
-                }
-            }
+            for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, o[u]);
         }
     }
 }
@@ -172,25 +177,24 @@ static uint32_t device_cus() {
     return (uint32_t)cus;
 }
 
-static Regime pick_regime(size_t nchunks_per_rank, int n) {
-    const size_t per_rank = nchunks_per_rank * 16;
-    const size_t working_set = per_rank * (size_t)(n + 1);
+// `working_set` is the bytes one call reads plus the bytes it writes.
+static Regime pick_regime(size_t nchunks_per_rank, size_t working_set) {
     if (working_set >= ((size_t)192 << 20)) return Regime::kStream;
     if (nchunks_per_rank >= (size_t)kBlock * 2 * 512) return Regime::kMid;
     return Regime::kSmall;
 }
 
-template <int N, int U, bool kStream, bool kSliced>
+template <int N, int U, bool kStream, Out kOut>
 static hipError_t go_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                             uint32_t slices, hipStream_t stream) {
     constexpr uint32_t kTile = kBlock * U;
     dim3 grid((nslice + kTile - 1) / kTile, slices);
     void* args[] = {&src, &dst, &nslice};
-    return hipLaunchKernel((const void*)&k_reduce<N, U, kStream, kSliced>, grid, dim3(kBlock), args,
+    return hipLaunchKernel((const void*)&k_reduce<N, U, kStream, kOut>, grid, dim3(kBlock), args,
                            0, stream);
 }
 
-template <int N, bool kSliced>
+template <int N, Out kOut>
 static hipError_t go_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                                        uint32_t slices, hipStream_t stream) {
     constexpr uint32_t kTile = kBlock * 4;
@@ -203,32 +207,32 @@ static hipError_t go_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
     const uint32_t rounds = (ntiles + slots - 1) / slots;
     const uint32_t grid = (ntiles + rounds - 1) / rounds;
     void* args[] = {&src, &dst, &nslice, &tiles_per_slice, &ntiles};
-    return hipLaunchKernel((const void*)&k_reduce_persistent<N, kSliced>, dim3(grid), dim3(kBlock),
+    return hipLaunchKernel((const void*)&k_reduce_persistent<N, kOut>, dim3(grid), dim3(kBlock),
                            args, 0, stream);
 }
 
-template <int N, bool kSliced>
+template <int N, Out kOut>
 static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                    uint32_t nslice, uint32_t slices, hipStream_t stream) {
     switch (rg) {
-        case Regime::kStream: return go_reduce_persistent<N, kSliced>(src, dst, nslice, slices, stream);
-        case Regime::kMid: return go_reduce<N, 2, false, kSliced>(src, dst, nslice, slices, stream);
-        default: return go_reduce<N, 1, false, kSliced>(src, dst, nslice, slices, stream);
+        case Regime::kStream: return go_reduce_persistent<N, kOut>(src, dst, nslice, slices, stream);
+        case Regime::kMid: return go_reduce<N, 2, false, kOut>(src, dst, nslice, slices, stream);
+        default: return go_reduce<N, 1, false, kOut>(src, dst, nslice, slices, stream);
     }
 }
 
-template <bool kSliced>
+template <Out kOut>
 static hipError_t dispatch_reduce(int n, Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                   uint32_t nslice, uint32_t slices, hipStream_t stream) {
     switch (n) {
-        case 1: return go_reduce_regime<1, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 2: return go_reduce_regime<2, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 3: return go_reduce_regime<3, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 4: return go_reduce_regime<4, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 5: return go_reduce_regime<5, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 6: return go_reduce_regime<6, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 7: return go_reduce_regime<7, kSliced>(rg, src, dst, nslice, slices, stream);
-        case 8: return go_reduce_regime<8, kSliced>(rg, src, dst, nslice, slices, stream);
+        case 1: return go_reduce_regime<1, kOut>(rg, src, dst, nslice, slices, stream);
+        case 2: return go_reduce_regime<2, kOut>(rg, src, dst, nslice, slices, stream);
+        case 3: return go_reduce_regime<3, kOut>(rg, src, dst, nslice, slices, stream);
+        case 4: return go_reduce_regime<4, kOut>(rg, src, dst, nslice, slices, stream);
+        case 5: return go_reduce_regime<5, kOut>(rg, src, dst, nslice, slices, stream);
+        case 6: return go_reduce_regime<6, kOut>(rg, src, dst, nslice, slices, stream);
+        case 7: return go_reduce_regime<7, kOut>(rg, src, dst, nslice, slices, stream);
+        case 8: return go_reduce_regime<8, kOut>(rg, src, dst, nslice, slices, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -256,7 +260,8 @@ hipError_t launch_reduce(const void* const* src, int n, void* out, size_t nchunk
     Ptrs<u32x4*> d = {};
     fill_src(s, src, n);
     d.p[0] = static_cast<u32x4*>(out);
-    return dispatch_reduce<false>(n, pick_regime(nchunks, n), s, d, (uint32_t)nchunks, 1, stream);
+    const Regime rg = pick_regime(nchunks, nchunks * 16 * (size_t)(n + 1));
+    return dispatch_reduce<Out::kOne>(n, rg, s, d, (uint32_t)nchunks, 1, stream);
 }
 
 hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size_t nchunks_slice,
@@ -265,8 +270,10 @@ hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size
     Ptrs<u32x4*> d = {};
     fill_src(s, src, n);
     for (int r = 0; r < n; ++r) d.p[r] = static_cast<u32x4*>(outs[r]);
-    const Regime rg = pick_regime(nchunks_slice * (size_t)n, n);
-    hipError_t e = dispatch_reduce<true>(n, rg, s, d, (uint32_t)nchunks_slice, (uint32_t)n, stream);
+    const size_t per_rank = nchunks_slice * (size_t)n;
+    const Regime rg = pick_regime(per_rank, per_rank * 16 * (size_t)(n + 1));
+    hipError_t e =
+        dispatch_reduce<Out::kOwner>(n, rg, s, d, (uint32_t)nchunks_slice, (uint32_t)n, stream);
     if (e != hipSuccess || n == 1) return e;
     const bool wide = rg != Regime::kSmall;
     switch (n) {
@@ -279,6 +286,22 @@ hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size
         case 8: return go_copyout<8>(d, (uint32_t)nchunks_slice, n, wide, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace pcdp
+
+namespace pcdp {
+
+hipError_t launch_twoshot_fused(const void* const* src, int n, void* const* outs,
+                                size_t nchunks_slice, hipStream_t stream) {
+    Ptrs<const u32x4*> s;
+    Ptrs<u32x4*> d = {};
+    fill_src(s, src, n);
+    for (int r = 0; r < n; ++r) d.p[r] = static_cast<u32x4*>(outs[r]);
+    // The fused call reads each input once and writes every output once.
+    const size_t per_rank = nchunks_slice * (size_t)n;
+    const Regime rg = pick_regime(per_rank, per_rank * 16 * 2 * (size_t)n);
+    return dispatch_reduce<Out::kAll>(n, rg, s, d, (uint32_t)nchunks_slice, (uint32_t)n, stream);
 }
 
 }  // namespace pcdp

@@ -65,7 +65,7 @@ enum {
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 1
+#define PC_ABI_VERSION 2
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -149,6 +149,24 @@ PC_API pc_status pc_consume_ll(const uint64_t* const* lines, int n, uint16_t* ou
  */
 PC_API pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
                      void* stream);
+
+/*
+ * pc_twoshot_fused -- twoshot in one launch: each owner block is folded once
+ * and distributed at once.
+ * Source: flash-comm, Section 4.3 (sharded two-hop: the two phases are linked
+ * per block, so an owner hands out a finished block while others are still in
+ * progress) and Section 3.3 (a block is computed once by its owner and
+ * distributed); Purlin, Section 3.1 (AllReduce composed from ReduceScatter
+ * and AllGather) and Listing 1 (compose: the second step consumes the
+ * first's intermediate in place, in one kernel).
+ * Same arguments, layouts, aliasing rules and errors as pc_twoshot, and the
+ * same result bit for bit: slice s = [s*k/n, (s+1)*k/n) is folded in rank
+ * order 0..n-1 exactly once, and the workgroup that folds a block writes it
+ * to every outs[r] (owner first).  One kernel is enqueued; the owner's slice
+ * is not read back.
+ */
+PC_API pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t* const* outs,
+                                  size_t k, void* stream);
 
 /*
  * pc_allgather_copy -- gather N shards of sequence-stamped blocks.

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.pc_abi_version() == 1
+    assert B.pc_abi_version() == 2
     assert B.pc_strerror(B.PC_OK) == "success"
     for st in (B.PC_EINVAL, B.PC_EALIGN, B.PC_EUNSUPPORTED, B.PC_EHIP, 12345):
         assert isinstance(B.pc_strerror(st), str) and B.pc_strerror(st)
@@ -118,6 +118,7 @@ def test_consume_validation(args, want):
 ])
 def test_twoshot_validation(args, want):
     assert B.pc_twoshot(stream=0, check=False, **args) == want
+    assert B.pc_twoshot_fused(stream=0, check=False, **args) == want
 
 
 @pytest.mark.parametrize("args,want", [

@@ -259,41 +259,45 @@ def test_consume_ll_wrong_seq_and_late_arrival(B, D, orc):
 
 # ---- twoshot -------------------------------------------------------------------
 
-def gpu_twoshot(B, D, xs):
+def gpu_twoshot(B, D, xs, fused=False):
     k = xs[0].size
     ins = [D.up(x) for x in xs]
     outs = [D.filled(k, 0xFFFF) for _ in xs]
-    B.pc_twoshot(ins, outs, k)
+    (B.pc_twoshot_fused if fused else B.pc_twoshot)(ins, outs, k)
     return [D.down(o, np.uint16) for o in outs]
 
 
-def test_twoshot_1m(B, D, orc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_twoshot_1m(B, D, orc, fused):
     case = synth.C3_TWOSHOT_1M
-    say(case.name)
+    say(case.name, "fused" if fused else "two launches")
     xs = case.inputs()
     want = orc.twoshot(xs)
-    got = gpu_twoshot(B, D, xs)
+    got = gpu_twoshot(B, D, xs, fused)
     oneshot = gpu_reduce(B, D, xs)
     for g, w in zip(got, want):
         assert np.array_equal(g, w)
         assert np.array_equal(g, oneshot)
 
 
-@pytest.mark.parametrize("n,slice_chunks", [(2, 1), (3, 257), (5, 256 * 4 + 3), (8, 300000 + 5), (1, 100)])
-def test_twoshot_shapes(B, D, orc, n, slice_chunks):
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("n,slice_chunks", [(2, 1), (3, 257), (5, 256 * 4 + 3), (8, 300000 + 5),
+                                            (1, 100), (6, 2 * 262144 + 9), (3, 100003)])
+def test_twoshot_shapes(B, D, orc, n, slice_chunks, fused):
     k = 8 * n * slice_chunks
-    say("twoshot", n, k)
+    say("twoshot", n, k, "fused" if fused else "")
     xs = [synth.normal_bf16(800 + n, 0, r, k) for r in range(n)]
     want = orc.reduce(xs, threads=THREADS)
-    for g in gpu_twoshot(B, D, xs):
+    for g in gpu_twoshot(B, D, xs, fused):
         assert np.array_equal(g, want)
 
 
-def test_twoshot_in_place(B, D, orc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_twoshot_in_place(B, D, orc, fused):
     n, k = 4, 8 * 4 * 999
     xs = [synth.normal_bf16(900, 0, r, k) for r in range(n)]
     ins = [D.up(x) for x in xs]
-    B.pc_twoshot(ins, ins, k)
+    (B.pc_twoshot_fused if fused else B.pc_twoshot)(ins, ins, k)
     want = orc.reduce(xs)
     for t in ins:
         assert np.array_equal(D.down(t, np.uint16), want)
