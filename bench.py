@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="timed calls of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
-                    choices=["all", "headline", "c1", "c2", "c3", "c5", "sweep", "copy"],
+                    choices=["all", "headline", "c1", "c2", "c2s", "c3", "c5", "sweep", "copy"],
                     help="run one part only (profiling); 'copy' times a plain device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -254,6 +254,57 @@ def run_c2(d, B, synth, oracle, args, out):
                                         and np.array_equal(d.down(bm, np.uint64), wb))
 
 
+def run_c2s(d, B, synth, oracle, args, out):
+    """Sentinel readiness next to LL at the same shape (8 ranks x 128 KiB).
+
+    Consuming re-arms sentinel slots, so a call cycle is timed: every rank
+    publishes (or packs), then the consumer consumes.  Parity is checked on
+    the workload with unarrived and torn packs and sentinel collisions."""
+    torch = d.torch
+    case = synth.C2S_SENTINEL_128K
+    xs = case.payloads()
+    src = [d.up(x) for x in xs]
+    slots = [torch.empty(case.k, dtype=torch.int16, device=d.dev) for _ in xs]
+    lines = [torch.empty(case.k // 2, dtype=torch.int64, device=d.dev) for _ in xs]
+    res = torch.empty(case.k, dtype=torch.int16, device=d.dev)
+    bm_s = torch.empty(case.k // 512, dtype=torch.int64, device=d.dev)
+    bm_l = torch.empty(case.k // 128, dtype=torch.int64, device=d.dev)
+
+    def sentinel_cycle():
+        for r in range(case.n):
+            B.pc_publish_sentinel(src[r], slots[r], case.k)
+        B.pc_consume_sentinel(slots, res, case.k, bm_s)
+
+    def ll_cycle():
+        for r in range(case.n):
+            B.pc_pack_ll(src[r], lines[r], case.k, 7)
+        B.pc_consume_ll(lines, res, case.k, 7, bm_l)
+
+    ts = timing(d, sentinel_cycle, 300, 20)
+    tl = timing(d, ll_cycle, 300, 20)
+    k = case.k
+    ts.update(workload="8 x publish + consume, all arrived, 8 ranks x 128 KiB",
+              staged_bytes_per_rank=2 * k, consume_bytes=case.n * 2 * k + 2 * k + case.n * 2 * k + k // 64)
+    tl.update(workload="8 x pack + consume, all current, 8 ranks x 128 KiB",
+              staged_bytes_per_rank=4 * k, consume_bytes=case.n * 4 * k + 2 * k + k // 16)
+    out["configs"]["sentinel_cycle_128k"] = ts
+    out["configs"]["ll_cycle_128k"] = tl
+    if oracle is not None:
+        ms = case.masks()
+        host = [synth.unarrive(oracle.publish_sentinel(x), m, t) for x, (m, t) in zip(xs, ms)]
+        for r in range(case.n):
+            B.pc_publish_sentinel(src[r], slots[r], case.k)
+        dev = [synth.unarrive(d.down(sl, np.uint16), m, t) for sl, (m, t) in zip(slots, ms)]
+        ok = all(np.array_equal(a, b) for a, b in zip(dev, host))
+        staged = [d.up(x) for x in dev]
+        res.fill_(-1)
+        B.pc_consume_sentinel(staged, res, case.k, bm_s)
+        wo, wb, wsl = oracle.consume_sentinel(host, case.k)
+        ok = ok and np.array_equal(d.down(res, np.uint16), wo) and np.array_equal(d.down(bm_s, np.uint64), wb)
+        ok = ok and all(np.array_equal(d.down(a, np.uint16), b) for a, b in zip(staged, wsl))
+        out["parity"]["sentinel_128k"] = bool(ok)
+
+
 def run_c3(d, B, synth, oracle, args, out):
     case = synth.C3_TWOSHOT_1M
     xs = case.inputs()
@@ -367,8 +418,8 @@ def main():
         headline_ms, ach = run_headline(d, B, synth, args, out)
     if args.only == "copy":
         run_copy(d, out, args.steps)
-    for name, fn in (("c1", run_c1), ("c2", run_c2), ("c3", run_c3), ("c5", run_c5),
-                     ("sweep", run_sweep)):
+    for name, fn in (("c1", run_c1), ("c2", run_c2), ("c2s", run_c2s), ("c3", run_c3),
+                     ("c5", run_c5), ("sweep", run_sweep)):
         if args.only in ("all", name):
             log("running", name)
             fn(d, B, synth, oracle, args, out)

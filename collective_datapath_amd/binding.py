@@ -22,7 +22,9 @@ PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
 EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_allgather_copy", "pc_strerror", "pc_abi_version")
+           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel", "pc_strerror",
+           "pc_abi_version")
+PC_SENTINEL = 0xFFFF
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -60,8 +62,10 @@ _lib.pc_consume_ll.argtypes = [_P, _I, _P, _S, ctypes.c_uint32, _P, _P]
 _lib.pc_twoshot.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_twoshot_fused.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
+_lib.pc_publish_sentinel.argtypes = [_P, _P, _S, _P]
+_lib.pc_consume_sentinel.argtypes = [_P, _I, _P, _S, _P, _P]
 for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_allgather_copy"):
+           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel"):
     getattr(_lib, _f).restype = _I
 _lib.pc_strerror.argtypes = [_I]
 _lib.pc_strerror.restype = ctypes.c_char_p
@@ -159,3 +163,15 @@ def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, s
     st = _lib.pc_allgather_copy(_addrs(shards), len(shards), _addr(out), shard_bytes, seq,
                                 _addr(ready_bitmap), _stream(stream))
     return _call("pc_allgather_copy", st, check)
+
+
+def pc_publish_sentinel(src: Buffer, slot: Buffer, k: int, stream=None, check: bool = True) -> int:
+    st = _lib.pc_publish_sentinel(_addr(src), _addr(slot), k, _stream(stream))
+    return _call("pc_publish_sentinel", st, check)
+
+
+def pc_consume_sentinel(slots: Sequence[Buffer], out: Buffer, k: int, ready_bitmap: Buffer,
+                        stream=None, check: bool = True) -> int:
+    st = _lib.pc_consume_sentinel(_addrs(slots), len(slots), _addr(out), k, _addr(ready_bitmap),
+                                  _stream(stream))
+    return _call("pc_consume_sentinel", st, check)

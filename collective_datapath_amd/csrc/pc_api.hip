@@ -174,6 +174,40 @@ pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
                                            static_cast<hipStream_t>(stream)));
 }
 
+pc_status pc_publish_sentinel(const uint16_t* src, uint16_t* slot, size_t k, void* stream) {
+    if (k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (k % 8) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (!src || !slot) return PC_EINVAL;
+    if (!aligned16(src) || !aligned16(slot)) return PC_EALIGN;
+    const size_t bytes = k * sizeof(uint16_t);
+    if (src != slot && overlaps(src, bytes, slot, bytes)) return PC_EINVAL;
+    return from_hip(pcdp::launch_publish_sentinel(src, slot, k / 8, static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_consume_sentinel(uint16_t* const* slots, int n, uint16_t* out, size_t k,
+                              uint64_t* ready_bitmap, void* stream) {
+    if (!valid_n(n) || !slots || k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (k % 512) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (pc_status st = check_ptrs(slots, n)) return st;
+    if (!out || !ready_bitmap) return PC_EINVAL;
+    if (!aligned16(out) || !aligned16(ready_bitmap)) return PC_EALIGN;
+    const size_t bytes = k * sizeof(uint16_t);
+    const size_t bm_bytes = (k / 512) * sizeof(uint64_t);
+    if (overlaps(out, bytes, ready_bitmap, bm_bytes)) return PC_EINVAL;
+    for (int a = 0; a < n; ++a) {
+        if (overlaps(slots[a], bytes, out, bytes) || overlaps(slots[a], bytes, ready_bitmap, bm_bytes))
+            return PC_EINVAL;
+        for (int b = a + 1; b < n; ++b)
+            if (overlaps(slots[a], bytes, slots[b], bytes)) return PC_EINVAL;
+    }
+    void* sp[PC_MAX_RANKS];
+    for (int r = 0; r < n; ++r) sp[r] = slots[r];
+    return from_hip(pcdp::launch_consume_sentinel(sp, n, out, k / 8, ready_bitmap,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 const char* pc_strerror(pc_status status) {
     switch (status) {
         case PC_OK: return "success";

@@ -35,6 +35,12 @@ hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t s
 hipError_t launch_consume_ll(const void* const* lines, int n, void* out, size_t nlines,
                              uint32_t seq, void* bitmap, hipStream_t stream);
 
+// Sentinel readiness: publish 16-byte chunks with substitution; consume
+// npacks 16-byte packs (a multiple of 64) from n slots, re-arming them.
+hipError_t launch_publish_sentinel(const void* src, void* dst, size_t nchunks, hipStream_t stream);
+hipError_t launch_consume_sentinel(void* const* slots, int n, void* out, size_t npacks,
+                                   void* bitmap, hipStream_t stream);
+
 // All-gather of n shards of `groups` 64-record groups each.
 hipError_t launch_allgather(const void* const* shards, int n, void* out, size_t groups,
                             uint64_t seq, void* bitmap, hipStream_t stream);

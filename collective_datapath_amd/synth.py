@@ -159,12 +159,73 @@ class GatherCase:
         return out, masks
 
 
+SENTINEL = 0xFFFF        # bf16 pattern reserved for "not yet arrived"
+PACK_ELEMS = 8           # readiness unit of sentinel storage: 16 bytes
+
+
+@dataclasses.dataclass(frozen=True)
+class SentinelCase:
+    """Sentinel readiness: per-rank payloads with some values equal to the
+    sentinel (so publication has to substitute them), packs that have not
+    arrived yet (still all sentinel) and torn packs (the upper half of the
+    pack still sentinel)."""
+    name: str
+    cfg: int
+    n: int
+    k: int
+    missing_frac: float = 0.05
+    torn_frac: float = 0.005
+    collision_frac: float = 0.01
+
+    @property
+    def packs(self) -> int:
+        return self.k // PACK_ELEMS
+
+    def payloads(self) -> List[np.ndarray]:
+        out = []
+        for r in range(self.n):
+            x = uniform_bf16(self.cfg, 0, r, self.k)
+            g = rng(self.cfg, 3, r)
+            hit = g.permutation(self.k)[: int(np.floor(self.collision_frac * self.k))]
+            x[hit] = SENTINEL
+            out.append(x)
+        return out
+
+    def masks(self) -> List[Tuple[np.ndarray, np.ndarray]]:
+        """(missing, torn) boolean masks over packs, disjoint, per rank."""
+        res = []
+        for r in range(self.n):
+            g = rng(self.cfg, 2, r)
+            perm = g.permutation(self.packs)
+            nm = int(np.floor(self.missing_frac * self.packs))
+            nt = int(np.floor(self.torn_frac * self.packs))
+            missing = np.zeros(self.packs, dtype=bool)
+            torn = np.zeros(self.packs, dtype=bool)
+            missing[perm[:nm]] = True
+            torn[perm[nm:nm + nt]] = True
+            res.append((missing, torn))
+        return res
+
+
+def unarrive(slot: np.ndarray, missing: np.ndarray, torn: np.ndarray) -> np.ndarray:
+    """Put the sentinel back where data has not arrived: whole missing packs,
+    and the upper half of torn packs.  Returns a new array."""
+    s = np.array(slot, dtype=np.uint16, copy=True).reshape(-1, PACK_ELEMS)
+    s[missing] = SENTINEL
+    s[torn, PACK_ELEMS // 2:] = SENTINEL
+    return s.reshape(-1)
+
+
 # The five workloads the datapath is measured and checked on.
 C1_ONESHOT_8K = ReduceCase("oneshot reduce N=4 K=1x4096 bf16 (8 KiB/rank)", 1, 4, 4096, "uniform")
 C2_LL_128K = LLCase("LL self-synchronizing reduce N=8 K=16x4096 bf16 (128 KiB/rank), 5% stale", 2, 8, 16 * 4096)
 C3_TWOSHOT_1M = ReduceCase("twoshot N=8 K=64x8192 bf16 (1 MiB/rank)", 3, 8, 64 * 8192, "normal", 1.0)
 C4_ONESHOT_64M = ReduceCase("oneshot reduce N=8 K=4096x8192 bf16 (64 MiB/rank)", 4, 8, 4096 * 8192, "normal", 0.02)
 C5_ALLGATHER_2M = GatherCase("all-gather copy N=8, 2 MiB shards in 136 B records, 10% stale", 5, 8, 2 * 1024 * 1024)
+
+# Sentinel-readiness consume at the LL workload's shape (compared against it).
+C2S_SENTINEL_128K = SentinelCase("sentinel self-synchronizing reduce N=8 K=16x4096 bf16 (128 KiB/rank), "
+                                 "5% packs unarrived, 0.5% torn", 6, 8, 16 * 4096)
 
 # Per-rank sizes of the latency sweep (bytes).
 SWEEP_BYTES = [8 << 10, 16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20]

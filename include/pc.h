@@ -65,7 +65,7 @@ enum {
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 2
+#define PC_ABI_VERSION 3
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -192,6 +192,45 @@ PC_API pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t
 PC_API pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
                             size_t shard_bytes, uint64_t seq, uint64_t* ready_bitmap,
                             void* stream);
+
+/*
+ * pc_publish_sentinel -- producer side of sentinel readiness.
+ * Source: flash-comm, Section 3.1 (sentinel readiness: storage is prefilled
+ * with a reserved pattern that a producer overwrites; a real value equal to
+ * the pattern is published as a canonical quiet NaN so it never looks
+ * unarrived).
+ *   src  : device, k bf16 values.
+ *   slot : device, k bf16; receives src with every 0xFFFF (PC_SENTINEL)
+ *          replaced by 0x7FC0.  May be exactly src (in place); any other
+ *          overlap is PC_EINVAL.  Written in 16-byte packs, one store each.
+ *   k    : multiple of 8, at most PC_MAX_ELEMS.
+ * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
+ */
+#define PC_SENTINEL 0xFFFFu
+#define PC_SENTINEL_PACK_ELEMS 8
+PC_API pc_status pc_publish_sentinel(const uint16_t* src, uint16_t* slot, size_t k, void* stream);
+
+/*
+ * pc_consume_sentinel -- consumer side: validate, fold and re-arm.
+ * Source: flash-comm, Section 3.1 (a pack that no longer holds the sentinel
+ * has arrived; the consumer restores the sentinel after capturing it) and
+ * Section 4.3 (one-hop: slots by source rank, fold only once every source has
+ * arrived, folded in rank order); Purlin, Section 3.3, Equation (2) (the fold).
+ *   slots : host array of n device pointers, k bf16 each, pairwise disjoint;
+ *           the receive storage of the n sources.  READ AND WRITTEN: every
+ *           pack that is consumed is re-armed (set back to 0xFFFF).
+ *   out   : device, k bf16.  Pack p (elements 8p..8p+7) is ready iff no
+ *           element of pack p holds 0xFFFF in any slot; then out[8p..8p+7] =
+ *           the rank-ordered fold, else out and the slots are left untouched.
+ *           No result element is ever 0xFFFF (NaN results are 0x7FC0).
+ *   k     : multiple of 512 (whole bitmap words), at most PC_MAX_ELEMS.
+ *   ready_bitmap : device, k/512 uint64 words; bit (p & 63) of word (p >> 6)
+ *           is 1 iff pack p was ready.  Every word is written.
+ *   out, ready_bitmap and the slots must not overlap one another.
+ * Errors: PC_EINVAL, PC_EALIGN (pointer alignment, k % 512 != 0), PC_EHIP.
+ */
+PC_API pc_status pc_consume_sentinel(uint16_t* const* slots, int n, uint16_t* out, size_t k,
+                                     uint64_t* ready_bitmap, void* stream);
 
 /* Static text for a status code (never NULL). */
 PC_API const char* pc_strerror(pc_status status);

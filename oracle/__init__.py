@@ -45,6 +45,10 @@ def lib() -> ctypes.CDLL:
         L.orc_twoshot.restype = I
         L.orc_allgather_copy.argtypes = [P, I, P, S, ctypes.c_uint64, P]
         L.orc_allgather_copy.restype = I
+        L.orc_publish_sentinel.argtypes = [P, P, S]
+        L.orc_publish_sentinel.restype = I
+        L.orc_consume_sentinel.argtypes = [P, I, P, S, P]
+        L.orc_consume_sentinel.restype = I
         _LIB = L
     return _LIB
 
@@ -133,3 +137,25 @@ def allgather_copy(shards: Sequence[np.ndarray], shard_bytes: int, seq: int,
     _check(lib().orc_allgather_copy(_ptr_array(ss), n, _ptr(out), shard_bytes, seq, _ptr(bitmap)),
            "orc_allgather_copy")
     return out, bitmap
+
+
+SENTINEL = 0xFFFF
+
+
+def publish_sentinel(src: np.ndarray) -> np.ndarray:
+    src = np.ascontiguousarray(src, dtype=np.uint16)
+    dst = np.empty_like(src)
+    _check(lib().orc_publish_sentinel(_ptr(src), _ptr(dst), src.size), "orc_publish_sentinel")
+    return dst
+
+
+def consume_sentinel(slots: Sequence[np.ndarray], k: int, out: Optional[np.ndarray] = None):
+    """Returns (out, bitmap, slots_after): the slots are copied, consumed and
+    re-armed; the caller's arrays are not modified."""
+    ss = [np.array(s, dtype=np.uint16, copy=True) for s in slots]
+    if out is None:
+        out = np.full(k, 0xFFFF, dtype=np.uint16)
+    bitmap = np.empty(k // 8 // 64, dtype=np.uint64)
+    _check(lib().orc_consume_sentinel(_ptr_array(ss), len(ss), _ptr(out), k, _ptr(bitmap)),
+           "orc_consume_sentinel")
+    return out, bitmap, ss

@@ -38,7 +38,10 @@
  *    bytes;
  *  - the ready bitmap is LSB-first u64 words: item i is bit (i & 63) of word
  *    (i >> 6);
- *  - output of a line or block that is not ready is left untouched.
+ *  - output of a line or block that is not ready is left untouched;
+ *  - the sentinel of sentinel readiness is the bf16 pattern 0xFFFF (a NaN),
+ *    the readiness unit is a pack of 8 bf16 (16 bytes), and a published value
+ *    equal to the sentinel is replaced by the canonical quiet NaN 0x7FC0.
  *
  * Floating point here is IEEE binary32 on x86-64 SSE2 (FLT_EVAL_METHOD 0),
  * built without -ffast-math and without contraction; orc_fpenv_ok() checks
@@ -258,6 +261,48 @@ int orc_allgather_copy(const uint8_t* const* shards, int n, uint8_t* out, size_t
             memcpy(out + item * 128, rec + 8, 128);
             bitmap[item / 64] |= (uint64_t)1 << (item % 64);
         }
+    }
+    return 0;
+}
+
+/* ---- sentinel readiness (flash-comm Section 3.1, Section 4.3) ----------- */
+
+#define ORC_SENTINEL 0xFFFFu
+#define ORC_CANON_NAN 0x7FC0u
+
+/* Producer: dst[i] = src[i], except that a value equal to the sentinel is
+ * published as the canonical quiet NaN, so real data never looks unarrived. */
+int orc_publish_sentinel(const uint16_t* src, uint16_t* dst, size_t k) {
+    for (size_t i = 0; i < k; ++i)
+        dst[i] = src[i] == ORC_SENTINEL ? (uint16_t)ORC_CANON_NAN : src[i];
+    return 0;
+}
+
+/* Consumer: pack p (elements 8p..8p+7) is ready iff no element of pack p in
+ * any rank's slot is the sentinel.  A ready pack is folded over ranks
+ * 0..n-1 into out and its slots are re-armed (every element set back to the
+ * sentinel); a pack that is not ready leaves out and the slots untouched.
+ * Bit p of the bitmap (LSB-first u64 words) is set to `ready`; every word is
+ * written.  k must be a multiple of 512 (whole bitmap words). */
+int orc_consume_sentinel(uint16_t* const* slots, int n, uint16_t* out, size_t k, uint64_t* bitmap) {
+    if (n < 1 || k % 512) return -1;
+    if (!mxcsr_ieee()) return -2;
+    size_t packs = k / 8;
+    for (size_t w = 0; w < packs / 64; ++w) bitmap[w] = 0;
+    for (size_t p = 0; p < packs; ++p) {
+        int ready = 1;
+        for (int r = 0; r < n; ++r)
+            for (size_t e = 8 * p; e < 8 * p + 8; ++e)
+                if (slots[r][e] == ORC_SENTINEL) ready = 0;
+        if (!ready) continue;
+        bitmap[p / 64] |= (uint64_t)1 << (p % 64);
+        for (size_t e = 8 * p; e < 8 * p + 8; ++e) {
+            float acc = -0.0f;
+            for (int r = 0; r < n; ++r) acc = acc + orc_widen(slots[r][e]);
+            out[e] = orc_narrow(acc);
+        }
+        for (int r = 0; r < n; ++r)
+            for (size_t e = 8 * p; e < 8 * p + 8; ++e) slots[r][e] = (uint16_t)ORC_SENTINEL;
     }
     return 0;
 }

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.pc_abi_version() == 2
+    assert B.pc_abi_version() == 3
     assert B.pc_strerror(B.PC_OK) == "success"
     for st in (B.PC_EINVAL, B.PC_EALIGN, B.PC_EUNSUPPORTED, B.PC_EHIP, 12345):
         assert isinstance(B.pc_strerror(st), str) and B.pc_strerror(st)
@@ -136,3 +136,29 @@ def test_allgather_validation(args, want):
 def test_one_hip_runtime_in_process():
     # The library must share torch's HIP runtime (streams, allocations).
     assert len(B._hip_runtimes()) == 1
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(src=A, slot=OUT, k=12), B.PC_EALIGN),
+    (dict(src=A + 8, slot=OUT, k=8), B.PC_EALIGN),
+    (dict(src=0, slot=OUT, k=8), B.PC_EINVAL),
+    (dict(src=A, slot=A + 16, k=64), B.PC_EINVAL),
+    (dict(src=A, slot=OUT, k=(1 << 34) + 8), B.PC_EINVAL),
+    (dict(src=A, slot=OUT, k=0), B.PC_OK),
+])
+def test_publish_sentinel_validation(args, want):
+    assert B.pc_publish_sentinel(stream=0, check=False, **args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(slots=ptrs(9), out=OUT, k=512, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(slots=ptrs(2), out=OUT, k=256, ready_bitmap=OUT + MB), B.PC_EALIGN),
+    (dict(slots=ptrs(2), out=OUT, k=512, ready_bitmap=0), B.PC_EINVAL),
+    (dict(slots=ptrs(2), out=OUT + 8, k=512, ready_bitmap=OUT + MB), B.PC_EALIGN),
+    (dict(slots=ptrs(2, stride=512), out=OUT, k=512, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(slots=ptrs(2), out=A + 512, k=512, ready_bitmap=OUT + MB), B.PC_EINVAL),
+    (dict(slots=ptrs(2), out=OUT, k=512, ready_bitmap=OUT + 512), B.PC_EINVAL),
+    (dict(slots=ptrs(2), out=OUT, k=0, ready_bitmap=0), B.PC_OK),
+])
+def test_consume_sentinel_validation(args, want):
+    assert B.pc_consume_sentinel(stream=0, check=False, **args) == want

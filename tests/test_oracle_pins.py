@@ -349,3 +349,77 @@ def test_allgather_stale_workload(orc):
     assert int(bits.sum()) == 131072 - 8 * 1638
     want = np.where(np.repeat(ready, 64), np.concatenate(case.payloads()), np.uint16(0xFFFF))
     assert np.array_equal(out, want)
+
+
+# --- sentinel readiness ----------------------------------------------------
+
+SENT = 0xFFFF
+
+
+def test_publish_sentinel_substitutes_only_the_sentinel(orc):
+    x = np.array([0xFFFF, 0x7FC0, 0xFFFE, 0x7FFF, 0x0000, 0x8000, 0xFFC0, 0x3F80], dtype=np.uint16)
+    assert [int(v) for v in orc.publish_sentinel(x)] == [0x7FC0, 0x7FC0, 0xFFFE, 0x7FFF, 0x0000,
+                                                         0x8000, 0xFFC0, 0x3F80]
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    p = orc.publish_sentinel(allh)
+    assert np.array_equal(p[allh != SENT], allh[allh != SENT]) and not np.any(p == SENT)
+
+
+def test_consume_sentinel_all_arrived_equals_reduce(orc):
+    case = synth.SentinelCase("all", 70, 5, 4096, 0.0, 0.0, 0.01)
+    xs = case.payloads()
+    assert any(np.any(x == SENT) for x in xs)
+    slots = [orc.publish_sentinel(x) for x in xs]
+    out, bm, after = orc.consume_sentinel(slots, case.k)
+    assert np.array_equal(out, lib_reduce(xs))          # a published sentinel is a NaN either way
+    assert np.all(bm == np.uint64(0xFFFFFFFFFFFFFFFF))
+    assert all(np.all(a == SENT) for a in after)        # every consumed slot re-armed
+
+
+def test_consume_sentinel_nothing_arrived(orc):
+    slots = [np.full(1024, SENT, np.uint16) for _ in range(3)]
+    out, bm, after = orc.consume_sentinel(slots, 1024)
+    assert np.all(bm == 0) and np.all(out == 0xFFFF)
+    assert all(np.all(a == SENT) for a in after)
+
+
+def test_consume_sentinel_torn_and_one_hot(orc):
+    n, k = 3, 1024
+    xs = [synth.uniform_bf16(71, 0, r, k) for r in range(n)]
+    slots = [orc.publish_sentinel(x) for x in xs]
+    slots[1] = slots[1].copy()
+    slots[1][8 * 70 + 7] = SENT                     # pack 70 torn on rank 1: word 1, bit 6
+    out, bm, after = orc.consume_sentinel(slots, k)
+    want_bm = np.full(2, 0xFFFFFFFFFFFFFFFF, dtype=np.uint64)
+    want_bm[1] &= ~np.uint64(1 << 6)
+    assert np.array_equal(bm, want_bm)
+    ref = lib_reduce(xs)
+    ref[8 * 70:8 * 71] = 0xFFFF
+    assert np.array_equal(out, ref)
+    for r in range(n):                               # the unready pack is not re-armed
+        assert np.array_equal(after[r][8 * 70:8 * 71], slots[r][8 * 70:8 * 71])
+        mask = np.ones(k, bool)
+        mask[8 * 70:8 * 71] = False
+        assert np.all(after[r][mask] == SENT)
+
+
+def test_consume_sentinel_workload_and_late_arrival(orc):
+    case = synth.C2S_SENTINEL_128K
+    xs = case.payloads()
+    ms = case.masks()
+    slots = [synth.unarrive(orc.publish_sentinel(x), m, t) for x, (m, t) in zip(xs, ms)]
+    out, bm, after = orc.consume_sentinel(slots, case.k)
+    bad = np.logical_or.reduce([m | t for m, t in ms])
+    bits = np.unpackbits(bm.view(np.uint8), bitorder="little").astype(bool)
+    assert np.array_equal(bits, ~bad)
+    ref = lib_reduce(xs)
+    assert np.array_equal(out, np.where(np.repeat(~bad, 8), ref, np.uint16(0xFFFF)))
+    assert not np.any(out[np.repeat(~bad, 8)] == SENT)
+    # The rest arrives: publish into the consumed storage (packs that were
+    # consumed are re-armed and get republished too), then consume again.
+    late = [np.where(np.repeat(~bad, 8), SENT, orc.publish_sentinel(x)).astype(np.uint16)
+            for x in xs]
+    out2, bm2, after2 = orc.consume_sentinel(late, case.k, out=out)
+    assert np.array_equal(np.unpackbits(bm2.view(np.uint8), bitorder="little").astype(bool), bad)
+    assert np.array_equal(out2, ref)
+    assert all(np.all(a == SENT) for a in after2)

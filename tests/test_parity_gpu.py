@@ -345,3 +345,83 @@ def test_allgather_header_compared_as_u64(B, D, orc):
     got_out, got_bm = gpu_allgather(B, D, recs, 2, 8192, case.seq)
     assert np.array_equal(got_bm, want_bm) and np.array_equal(got_out, want_out)
     assert int(np.unpackbits(got_bm.view(np.uint8)).sum()) == 127
+
+
+# ---- sentinel readiness -------------------------------------------------------------
+
+def gpu_publish(B, D, x):
+    src = D.up(x)
+    slot = torch.empty_like(src)
+    B.pc_publish_sentinel(src, slot, x.size)
+    return slot
+
+
+def gpu_consume_sentinel(B, D, slots_dev, k, out_fill=0xFFFF):
+    out = D.filled(k, out_fill)
+    bm = torch.full((k // 512,), -1, dtype=torch.int64, device="cuda:0")
+    B.pc_consume_sentinel(slots_dev, out, k, bm)
+    return D.down(out, np.uint16), D.down(bm, np.uint64), [D.down(s, np.uint16) for s in slots_dev]
+
+
+def test_publish_sentinel_bits(B, D, orc):
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    assert np.array_equal(D.down(gpu_publish(B, D, allh), np.uint16), orc.publish_sentinel(allh))
+    x = synth.SentinelCase("pub", 72, 1, 8 * 777).payloads()[0]
+    assert np.array_equal(D.down(gpu_publish(B, D, x), np.uint16), orc.publish_sentinel(x))
+    t = D.up(x)                                          # in place
+    B.pc_publish_sentinel(t, t, x.size)
+    assert np.array_equal(D.down(t, np.uint16), orc.publish_sentinel(x))
+
+
+def test_consume_sentinel_128k_workload(B, D, orc):
+    case = synth.C2S_SENTINEL_128K
+    say(case.name)
+    xs, ms = case.payloads(), case.masks()
+    # Each side publishes with its own code; unarrived/torn packs are then
+    # put back to the sentinel by the harness.
+    dev = [synth.unarrive(D.down(gpu_publish(B, D, x), np.uint16), m, t) for x, (m, t) in zip(xs, ms)]
+    host = [synth.unarrive(orc.publish_sentinel(x), m, t) for x, (m, t) in zip(xs, ms)]
+    for a, b in zip(dev, host):
+        assert np.array_equal(a, b)
+    want_out, want_bm, want_slots = orc.consume_sentinel(host, case.k)
+    got_out, got_bm, got_slots = gpu_consume_sentinel(B, D, [D.up(s) for s in dev], case.k)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+    for g, w in zip(got_slots, want_slots):
+        assert np.array_equal(g, w)
+    ready = int(np.unpackbits(got_bm.view(np.uint8)).sum())
+    assert 0.6 * case.packs < ready < 0.7 * case.packs
+
+
+@pytest.mark.parametrize("n,k", [(1, 512), (2, 512 * 3), (3, 512 * 37), (5, 512 * 129), (8, 1 << 20)])
+def test_consume_sentinel_shapes(B, D, orc, n, k):
+    case = synth.SentinelCase("shape", 73 + n, n, k, 0.03, 0.01, 0.01)
+    slots = [synth.unarrive(orc.publish_sentinel(x), m, t)
+             for x, (m, t) in zip(case.payloads(), case.masks())]
+    want_out, want_bm, want_slots = orc.consume_sentinel(slots, k)
+    got_out, got_bm, got_slots = gpu_consume_sentinel(B, D, [D.up(s) for s in slots], k)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+    assert all(np.array_equal(g, w) for g, w in zip(got_slots, want_slots))
+
+
+def test_consume_sentinel_late_arrival(B, D, orc):
+    case = synth.SentinelCase("late", 80, 8, 8192)
+    xs, ms = case.payloads(), case.masks()
+    slots = [D.up(synth.unarrive(orc.publish_sentinel(x), m, t)) for x, (m, t) in zip(xs, ms)]
+    out = D.filled(case.k, 0xFFFF)
+    bm = torch.empty(case.k // 512, dtype=torch.int64, device="cuda:0")
+    B.pc_consume_sentinel(slots, out, case.k, bm)
+    first = D.down(bm, np.uint64).copy()
+    # The producers now publish everything; packs consumed in the first round
+    # are published again into their re-armed storage.
+    done = np.repeat(np.unpackbits(first.view(np.uint8), bitorder="little").astype(bool), 8)
+    for s, x in zip(slots, xs):
+        fresh = D.down(gpu_publish(B, D, x), np.uint16)
+        cur = D.down(s, np.uint16)
+        s.copy_(D.up(np.where(done, cur, fresh).astype(np.uint16)))
+    B.pc_consume_sentinel(slots, out, case.k, bm)
+    second = D.down(bm, np.uint64)
+    assert np.all((first | second) == np.uint64(0xFFFFFFFFFFFFFFFF)) and np.all((first & second) == 0)
+    assert np.array_equal(D.down(out, np.uint16), orc.reduce(xs))
+    assert all(np.all(D.down(s, np.uint16) == 0xFFFF) for s in slots)
