@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="timed calls of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
-                    choices=["all", "headline", "c1", "c2", "c2s", "c3", "c5", "sweep", "copy"],
+                    choices=["all", "headline", "c1", "c1v", "c2", "c2s", "c3", "c5", "sweep",
+                             "copy"],
                     help="run one part only (profiling); 'copy' times a plain device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -305,6 +306,36 @@ def run_c2s(d, B, synth, oracle, args, out):
         out["parity"]["sentinel_128k"] = bool(ok)
 
 
+def run_c1v(d, B, synth, oracle, args, out):
+    """Speculative reduce at decode size: validation passes on the first
+    attempt; then the cost of one retry, from a flag that never validates."""
+    torch = d.torch
+    case = synth.C1V_VALIDATED_8K
+    xs, fl = case.payloads(), case.flags()
+    ins = [d.up(x) for x in xs]
+    flags = [torch.from_numpy(f.view(np.int32)).to(d.dev) for f in fl]
+    res = torch.full((case.k,), -1, dtype=torch.int16, device=d.dev)
+    at = torch.empty(case.tiles, dtype=torch.int32, device=d.dev)
+    t = timing(d, lambda: B.pc_reduce_validated(ins, flags, res, case.k, case.elems_per_flag,
+                                                case.flag, 1, at), 2000, 100)
+    t.update(workload=case.name, bytes_per_call=(case.n + 1) * 2 * case.k + 4 * case.n * case.tiles)
+    out["configs"]["validated_8k"] = t
+    if oracle is not None:
+        wo, wok = oracle.reduce_validated(xs, fl, case.elems_per_flag, case.flag)
+        out["parity"]["validated_8k"] = bool(np.array_equal(d.down(res, np.uint16), wo) and
+                                             np.array_equal(d.down(at, np.uint32), wok))
+    stale = [f.clone() for f in flags]
+    stale[0].sub_(1)
+    t1 = d.graph_us(lambda: B.pc_reduce_validated(ins, stale, res, case.k, case.elems_per_flag,
+                                                  case.flag, 1, at))
+    t9 = d.graph_us(lambda: B.pc_reduce_validated(ins, stale, res, case.k, case.elems_per_flag,
+                                                  case.flag, 9, at))
+    out["configs"]["validated_8k_retry"] = {
+        "workload": "same call with one stale flag: 1 vs 9 attempts",
+        "graph_us_1_attempt": round(t1, 3), "graph_us_9_attempts": round(t9, 3),
+        "us_per_retry": round((t9 - t1) / 8, 3)}
+
+
 def run_c3(d, B, synth, oracle, args, out):
     case = synth.C3_TWOSHOT_1M
     xs = case.inputs()
@@ -418,7 +449,7 @@ def main():
         headline_ms, ach = run_headline(d, B, synth, args, out)
     if args.only == "copy":
         run_copy(d, out, args.steps)
-    for name, fn in (("c1", run_c1), ("c2", run_c2), ("c2s", run_c2s), ("c3", run_c3),
+    for name, fn in (("c1", run_c1), ("c1v", run_c1v), ("c2", run_c2), ("c2s", run_c2s), ("c3", run_c3),
                      ("c5", run_c5), ("sweep", run_sweep)):
         if args.only in ("all", name):
             log("running", name)

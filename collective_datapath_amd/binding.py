@@ -22,8 +22,9 @@ PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
 EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel", "pc_strerror",
-           "pc_abi_version")
+           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
+           "pc_reduce_validated", "pc_strerror", "pc_abi_version")
+PC_MAX_ATTEMPTS = 65536
 PC_SENTINEL = 0xFFFF
 
 if not os.path.exists(LIB_PATH):
@@ -63,9 +64,11 @@ _lib.pc_twoshot.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_twoshot_fused.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
 _lib.pc_publish_sentinel.argtypes = [_P, _P, _S, _P]
+_lib.pc_reduce_validated.argtypes = [_P, _P, _I, _P, _S, _S, ctypes.c_uint32, ctypes.c_uint32, _P, _P]
 _lib.pc_consume_sentinel.argtypes = [_P, _I, _P, _S, _P, _P]
 for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel"):
+           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
+           "pc_reduce_validated"):
     getattr(_lib, _f).restype = _I
 _lib.pc_strerror.argtypes = [_I]
 _lib.pc_strerror.restype = ctypes.c_char_p
@@ -175,3 +178,14 @@ def pc_consume_sentinel(slots: Sequence[Buffer], out: Buffer, k: int, ready_bitm
     st = _lib.pc_consume_sentinel(_addrs(slots), len(slots), _addr(out), k, _addr(ready_bitmap),
                                   _stream(stream))
     return _call("pc_consume_sentinel", st, check)
+
+
+def pc_reduce_validated(inputs: Sequence[Buffer], flags: Sequence[Buffer], out: Buffer, k: int,
+                        elems_per_flag: int, flag: int, max_attempts: int, attempts: Buffer,
+                        stream=None, check: bool = True) -> int:
+    if len(flags) != len(inputs):
+        raise ValueError("pc_reduce_validated needs one flag buffer per input")
+    st = _lib.pc_reduce_validated(_addrs(inputs), _addrs(flags), len(inputs), _addr(out), k,
+                                  elems_per_flag, flag & 0xFFFFFFFF, max_attempts, _addr(attempts),
+                                  _stream(stream))
+    return _call("pc_reduce_validated", st, check)

@@ -46,6 +46,8 @@ pc_status check_ptrs(const T* const* ptrs, int n) {
 
 inline pc_status from_hip(hipError_t e) { return e == hipSuccess ? PC_OK : PC_EHIP; }
 
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -172,6 +174,42 @@ pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
     for (int r = 0; r < n; ++r) src[r] = shards[r];
     return from_hip(pcdp::launch_allgather(src, n, out, blocks / 64, seq, ready_bitmap,
                                            static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_reduce_validated(const uint16_t* const* inputs, const uint32_t* const* flags, int n,
+                              uint16_t* out, size_t k, size_t elems_per_flag, uint32_t flag,
+                              uint32_t max_attempts, uint32_t* attempts, void* stream) {
+    if (!valid_n(n) || !inputs || !flags || k > PC_MAX_ELEMS) return PC_EINVAL;
+    if (max_attempts < 1 || max_attempts > PC_MAX_ATTEMPTS) return PC_EINVAL;
+    if (elems_per_flag == 0 || elems_per_flag % 2048 || elems_per_flag > 4 * 2048) return PC_EINVAL;
+    if (k % elems_per_flag) return PC_EALIGN;
+    if (k == 0) return PC_OK;
+    if (pc_status st = check_ptrs(inputs, n)) return st;
+    for (int r = 0; r < n; ++r)
+        if (!flags[r]) return PC_EINVAL;
+    for (int r = 0; r < n; ++r)
+        if (!aligned4(flags[r])) return PC_EALIGN;
+    if (!out || !attempts) return PC_EINVAL;
+    if (!aligned16(out) || !aligned4(attempts)) return PC_EALIGN;
+    const size_t bytes = k * sizeof(uint16_t);
+    const size_t tiles = k / elems_per_flag;
+    const size_t tbytes = tiles * sizeof(uint32_t);
+    if (overlaps(out, bytes, attempts, tbytes)) return PC_EINVAL;
+    for (int r = 0; r < n; ++r) {
+        if (inputs[r] != out && overlaps(inputs[r], bytes, out, bytes)) return PC_EINVAL;
+        if (overlaps(inputs[r], bytes, attempts, tbytes) || overlaps(flags[r], tbytes, attempts, tbytes) ||
+            overlaps(flags[r], tbytes, out, bytes))
+            return PC_EINVAL;
+    }
+    const void* src[PC_MAX_RANKS];
+    const void* fl[PC_MAX_RANKS];
+    for (int r = 0; r < n; ++r) {
+        src[r] = inputs[r];
+        fl[r] = flags[r];
+    }
+    return from_hip(pcdp::launch_reduce_validated(src, fl, n, out, k, elems_per_flag, flag,
+                                                  max_attempts, attempts,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 pc_status pc_publish_sentinel(const uint16_t* src, uint16_t* slot, size_t k, void* stream) {

@@ -41,6 +41,12 @@ hipError_t launch_publish_sentinel(const void* src, void* dst, size_t nchunks, h
 hipError_t launch_consume_sentinel(void* const* slots, int n, void* out, size_t npacks,
                                    void* bitmap, hipStream_t stream);
 
+// Speculative reduce, one workgroup per validation tile of elems_per_flag
+// (2048, 4096, 6144 or 8192) elements.
+hipError_t launch_reduce_validated(const void* const* src, const void* const* flags, int n,
+                                   void* out, size_t k, size_t elems_per_flag, uint32_t flag,
+                                   uint32_t max_attempts, void* attempts, hipStream_t stream);
+
 // All-gather of n shards of `groups` 64-record groups each.
 hipError_t launch_allgather(const void* const* shards, int n, void* out, size_t groups,
                             uint64_t seq, void* bitmap, hipStream_t stream);

@@ -207,6 +207,35 @@ class SentinelCase:
         return res
 
 
+@dataclasses.dataclass(frozen=True)
+class ValidatedCase:
+    """Speculative reduce: payloads plus one validation flag per tile per rank.
+    A stale tile on a rank carries the previous call's flag (flag - 1)."""
+    name: str
+    cfg: int
+    n: int
+    k: int
+    elems_per_flag: int
+    flag: int = 5
+    stale_frac: float = 0.05
+
+    @property
+    def tiles(self) -> int:
+        return self.k // self.elems_per_flag
+
+    def payloads(self) -> List[np.ndarray]:
+        return [uniform_bf16(self.cfg, 0, r, self.k) for r in range(self.n)]
+
+    def flags(self) -> List[np.ndarray]:
+        out = []
+        for r in range(self.n):
+            m = stale_mask(self.cfg, r, self.tiles, self.stale_frac)
+            f = np.full(self.tiles, self.flag & 0xFFFFFFFF, dtype=np.uint32)
+            f[m] = np.uint32((self.flag - 1) & 0xFFFFFFFF)
+            out.append(f)
+        return out
+
+
 def unarrive(slot: np.ndarray, missing: np.ndarray, torn: np.ndarray) -> np.ndarray:
     """Put the sentinel back where data has not arrived: whole missing packs,
     and the upper half of torn packs.  Returns a new array."""
@@ -226,6 +255,10 @@ C5_ALLGATHER_2M = GatherCase("all-gather copy N=8, 2 MiB shards in 136 B records
 # Sentinel-readiness consume at the LL workload's shape (compared against it).
 C2S_SENTINEL_128K = SentinelCase("sentinel self-synchronizing reduce N=8 K=16x4096 bf16 (128 KiB/rank), "
                                  "5% packs unarrived, 0.5% torn", 6, 8, 16 * 4096)
+
+# Speculative reduce at decode size: 8 ranks x 8 KiB, one flag per 4096 elements.
+C1V_VALIDATED_8K = ValidatedCase("speculative reduce N=8 K=1x4096 bf16 (8 KiB/rank), one flag", 7, 8, 4096, 4096,
+                                 stale_frac=0.0)
 
 # Per-rank sizes of the latency sweep (bytes).
 SWEEP_BYTES = [8 << 10, 16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20]

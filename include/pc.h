@@ -65,7 +65,7 @@ enum {
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 3
+#define PC_ABI_VERSION 4
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -192,6 +192,39 @@ PC_API pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t
 PC_API pc_status pc_allgather_copy(const uint8_t* const* shards, int n, uint16_t* out,
                             size_t shard_bytes, uint64_t seq, uint64_t* ready_bitmap,
                             void* stream);
+
+/*
+ * pc_reduce_validated -- speculative reduce checked by a folded flag.
+ * Source: SiFAR, Section 4 (paragraphs on eliminating flag exchange, on the
+ * verification logic with Figure 14, and on speculative reduction): each
+ * rank writes the call's flag into its validation buffer before the
+ * reduction; the consumer reduces the flags (integer sum) next to the
+ * payload and accepts iff the sum equals n * flag, rerunning otherwise.
+ *   inputs  : host array of n device pointers, k bf16 each (may alias).
+ *   flags   : host array of n device pointers, k/elems_per_flag uint32 each,
+ *             4-byte aligned; word b of rank r validates tile b.
+ *   out     : device, k bf16.  Tile b = elements [b*t, (b+1)*t), t =
+ *             elems_per_flag.  A tile whose folded flag (sum mod 2^32 over
+ *             ranks) equals n*flag (mod 2^32) is folded in rank order 0..n-1
+ *             into out; a tile that never validates leaves out untouched.
+ *             out may be exactly one input; other overlaps are PC_EINVAL.
+ *   elems_per_flag : 2048, 4096, 6144 or 8192; k must be a multiple of it.
+ *   flag    : the current call's flag (callers advance it every call and
+ *             alternate two validation buffers, as the pages do).
+ *   max_attempts : 1..PC_MAX_ATTEMPTS.  A tile that fails the check is
+ *             re-read (flags and payload, past the caches) up to this many
+ *             times in total; the bound makes every call finish.
+ *   attempts: device, k/elems_per_flag uint32: the attempt that validated
+ *             tile b (1-based), or 0.  Every word is written.
+ * Flags and payload are read in the same attempt without ordering; as on
+ * the pages, the check is sound when ranks progress monotonically.
+ * Errors: PC_EINVAL, PC_EALIGN, PC_EHIP.
+ */
+#define PC_MAX_ATTEMPTS 65536u
+PC_API pc_status pc_reduce_validated(const uint16_t* const* inputs, const uint32_t* const* flags,
+                                     int n, uint16_t* out, size_t k, size_t elems_per_flag,
+                                     uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
+                                     void* stream);
 
 /*
  * pc_publish_sentinel -- producer side of sentinel readiness.

@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.orc_twoshot.restype = I
         L.orc_allgather_copy.argtypes = [P, I, P, S, ctypes.c_uint64, P]
         L.orc_allgather_copy.restype = I
+        L.orc_reduce_validated.argtypes = [P, P, I, P, S, S, ctypes.c_uint32, P]
+        L.orc_reduce_validated.restype = I
         L.orc_publish_sentinel.argtypes = [P, P, S]
         L.orc_publish_sentinel.restype = I
         L.orc_consume_sentinel.argtypes = [P, I, P, S, P]
@@ -159,3 +161,17 @@ def consume_sentinel(slots: Sequence[np.ndarray], k: int, out: Optional[np.ndarr
     _check(lib().orc_consume_sentinel(_ptr_array(ss), len(ss), _ptr(out), k, _ptr(bitmap)),
            "orc_consume_sentinel")
     return out, bitmap, ss
+
+
+def reduce_validated(inputs: Sequence[np.ndarray], flags: Sequence[np.ndarray], elems_per_flag: int,
+                     flag: int, out: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in inputs]
+    fs = [np.ascontiguousarray(f, dtype=np.uint32) for f in flags]
+    k = xs[0].size
+    if out is None:
+        out = np.full(k, 0xFFFF, dtype=np.uint16)
+    ok = np.empty(k // elems_per_flag, dtype=np.uint32)
+    _check(lib().orc_reduce_validated(_ptr_array(xs), _ptr_array(fs), len(xs), _ptr(out), k,
+                                      elems_per_flag, flag & 0xFFFFFFFF, _ptr(ok)),
+           "orc_reduce_validated")
+    return out, ok

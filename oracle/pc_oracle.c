@@ -306,3 +306,31 @@ int orc_consume_sentinel(uint16_t* const* slots, int n, uint16_t* out, size_t k,
     }
     return 0;
 }
+
+/* ---- speculative reduce with a folded validation flag -------------------- */
+/* "SiFAR: Synchronization-Free All-Reduce for Low-Latency LLM Inference",
+ * Section 4 (the paragraphs on eliminating flag exchange, on the verification
+ * logic with Figure 14, and on speculative reduction): every rank writes the call's flag into
+ * its validation buffer; the validation buffers are reduced (an integer sum
+ * over ranks) next to the payload, and the result is accepted iff the folded
+ * flag equals n * flag.  Tile b covers elements [b*t, (b+1)*t) with t =
+ * elems_per_flag and is validated by flag word b of every rank.  With the
+ * inputs fixed, the first attempt decides: ok[b] = 1 and the tile is folded
+ * into out when the check passes, else ok[b] = 0 and out is untouched.  The
+ * sum and the product wrap modulo 2^32. */
+int orc_reduce_validated(const uint16_t* const* inputs, const uint32_t* const* flags, int n,
+                         uint16_t* out, size_t k, size_t elems_per_flag, uint32_t flag,
+                         uint32_t* ok) {
+    if (n < 1 || elems_per_flag == 0 || k % elems_per_flag) return -1;
+    if (!mxcsr_ieee()) return -2;
+    size_t tiles = k / elems_per_flag;
+    for (size_t b = 0; b < tiles; ++b) {
+        uint32_t folded = 0;
+        for (int r = 0; r < n; ++r) folded += flags[r][b];
+        ok[b] = folded == (uint32_t)n * flag;
+        if (!ok[b]) continue;
+        for (size_t i = b * elems_per_flag; i < (b + 1) * elems_per_flag; ++i)
+            out[i] = orc_narrow(fold_element(inputs, n, NULL, i));
+    }
+    return 0;
+}

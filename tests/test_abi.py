@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.pc_abi_version() == 3
+    assert B.pc_abi_version() == 4
     assert B.pc_strerror(B.PC_OK) == "success"
     for st in (B.PC_EINVAL, B.PC_EALIGN, B.PC_EUNSUPPORTED, B.PC_EHIP, 12345):
         assert isinstance(B.pc_strerror(st), str) and B.pc_strerror(st)
@@ -162,3 +162,32 @@ def test_publish_sentinel_validation(args, want):
 ])
 def test_consume_sentinel_validation(args, want):
     assert B.pc_consume_sentinel(stream=0, check=False, **args) == want
+
+
+FL = A + 2048 * MB
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=2048, elems_per_flag=2048, flag=1,
+          max_attempts=0, attempts=OUT + MB), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=2048, elems_per_flag=2048, flag=1,
+          max_attempts=65537, attempts=OUT + MB), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=4096, elems_per_flag=1024, flag=1,
+          max_attempts=1, attempts=OUT + MB), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=4096, elems_per_flag=16384, flag=1,
+          max_attempts=1, attempts=OUT + MB), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=6144, elems_per_flag=4096, flag=1,
+          max_attempts=1, attempts=OUT + MB), B.PC_EALIGN),
+    (dict(inputs=ptrs(2), flags=[FL, FL + 2], out=OUT, k=2048, elems_per_flag=2048, flag=1,
+          max_attempts=1, attempts=OUT + MB), B.PC_EALIGN),
+    (dict(inputs=ptrs(2), flags=[FL, 0], out=OUT, k=2048, elems_per_flag=2048, flag=1,
+          max_attempts=1, attempts=OUT + MB), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=2048, elems_per_flag=2048, flag=1,
+          max_attempts=1, attempts=OUT + 64), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=2048, elems_per_flag=2048, flag=1,
+          max_attempts=1, attempts=FL), B.PC_EINVAL),
+    (dict(inputs=ptrs(2), flags=ptrs(2, base=FL), out=OUT, k=0, elems_per_flag=2048, flag=1,
+          max_attempts=1, attempts=0), B.PC_OK),
+])
+def test_reduce_validated_validation(args, want):
+    assert B.pc_reduce_validated(stream=0, check=False, **args) == want

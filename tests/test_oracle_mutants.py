@@ -44,6 +44,10 @@ MUTANTS = {
     "all-gather record stride": [("const uint8_t* rec = shards[r] + 136 * b;", "const uint8_t* rec = shards[r] + 128 * b;")],
     "all-gather header low word only": [("if (header != seq) continue;", "if ((uint32_t)header != (uint32_t)seq) continue;")],
     "all-gather output transposed": [("size_t item = (size_t)r * blocks + b;", "size_t item = (size_t)b * n + r;")],
+    "validation compares each flag": [("for (int r = 0; r < n; ++r) folded += flags[r][b];\n        ok[b] = folded == (uint32_t)n * flag;", "int each = 1;\n        for (int r = 0; r < n; ++r) { folded += flags[r][b]; each &= flags[r][b] == flag; }\n        ok[b] = each;")],
+    "validation without the rank count": [("ok[b] = folded == (uint32_t)n * flag;", "ok[b] = folded == flag;")],
+    "validation reads tile 0's flags": [("folded += flags[r][b];", "folded += flags[r][0];")],
+    "validation writes rejected tiles": [("        ok[b] = folded == (uint32_t)n * flag;\n        if (!ok[b]) continue;", "        ok[b] = folded == (uint32_t)n * flag;")],
     "sentinel not substituted": [("dst[i] = src[i] == ORC_SENTINEL ? (uint16_t)ORC_CANON_NAN : src[i];", "dst[i] = src[i];")],
     "sentinel checked on first element only": [("for (size_t e = 8 * p; e < 8 * p + 8; ++e)\n                if (slots[r][e] == ORC_SENTINEL) ready = 0;", "for (size_t e = 8 * p; e < 8 * p + 1; ++e)\n                if (slots[r][e] == ORC_SENTINEL) ready = 0;")],
     "sentinel slots not re-armed": [("for (size_t e = 8 * p; e < 8 * p + 8; ++e) slots[r][e] = (uint16_t)ORC_SENTINEL;", "for (size_t e = 8 * p; e < 8 * p; ++e) slots[r][e] = (uint16_t)ORC_SENTINEL;")],

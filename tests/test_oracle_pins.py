@@ -423,3 +423,57 @@ def test_consume_sentinel_workload_and_late_arrival(orc):
     assert np.array_equal(np.unpackbits(bm2.view(np.uint8), bitorder="little").astype(bool), bad)
     assert np.array_equal(out2, ref)
     assert all(np.all(a == SENT) for a in after2)
+
+
+# --- speculative reduce with a folded validation flag ----------------------
+
+def test_validated_all_current_equals_reduce(orc):
+    case = synth.ValidatedCase("ok", 74, 6, 8192, 2048, flag=9, stale_frac=0.0)
+    xs = case.payloads()
+    out, ok = orc.reduce_validated(xs, case.flags(), 2048, 9)
+    assert np.all(ok == 1)
+    assert np.array_equal(out, lib_reduce(xs))
+
+
+def test_validated_stale_tile_rejected(orc):
+    n, k, t = 4, 8192, 2048
+    xs = [synth.uniform_bf16(75, 0, r, k) for r in range(n)]
+    flags = [np.full(k // t, 3, np.uint32) for _ in range(n)]
+    flags[2][1] = 2                                      # rank 2 has not reached this call on tile 1
+    out, ok = orc.reduce_validated(xs, flags, t, 3)
+    assert [int(v) for v in ok] == [1, 0, 1, 1]
+    ref = lib_reduce(xs)
+    ref[t:2 * t] = 0xFFFF
+    assert np.array_equal(out, ref)
+
+
+def test_validated_folds_flags_rather_than_comparing_each(orc):
+    # The check compares the folded (summed) flag with n * flag: errors that
+    # cancel in the sum pass it.  The pages rely on monotonic progress of the
+    # ranks to rule such states out; the rule itself is what is pinned here.
+    n, k, t = 3, 2048, 2048
+    xs = [synth.uniform_bf16(76, 0, r, k) for r in range(n)]
+    flags = [np.array([6], np.uint32), np.array([8], np.uint32), np.array([7], np.uint32)]
+    out, ok = orc.reduce_validated(xs, flags, t, 7)
+    assert int(ok[0]) == 1 and np.array_equal(out, lib_reduce(xs))
+
+
+def test_validated_flag_arithmetic_wraps(orc):
+    n, k = 8, 2048
+    xs = [synth.uniform_bf16(77, 0, r, k) for r in range(n)]
+    top = 0xFFFFFFFF
+    out, ok = orc.reduce_validated(xs, [np.array([top], np.uint32)] * n, k, top)
+    assert int(ok[0]) == 1
+    flags = [np.array([top], np.uint32)] * (n - 1) + [np.array([0], np.uint32)]
+    out, ok = orc.reduce_validated(xs, flags, k, top)
+    assert int(ok[0]) == 0 and np.all(out == 0xFFFF)
+
+
+def test_validated_workload_popcount(orc):
+    case = synth.ValidatedCase("stale", 78, 8, 64 * 2048, 2048, flag=11, stale_frac=0.05)
+    fl = case.flags()
+    out, ok = orc.reduce_validated(case.payloads(), fl, 2048, 11)
+    good = np.logical_and.reduce([f == 11 for f in fl])
+    assert np.array_equal(ok.astype(bool), good)
+    ref = lib_reduce(case.payloads())
+    assert np.array_equal(out, np.where(np.repeat(good, 2048), ref, np.uint16(0xFFFF)))

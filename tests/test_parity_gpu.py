@@ -425,3 +425,60 @@ def test_consume_sentinel_late_arrival(B, D, orc):
     assert np.all((first | second) == np.uint64(0xFFFFFFFFFFFFFFFF)) and np.all((first & second) == 0)
     assert np.array_equal(D.down(out, np.uint16), orc.reduce(xs))
     assert all(np.all(D.down(s, np.uint16) == 0xFFFF) for s in slots)
+
+
+
+# ---- speculative reduce with a folded validation flag ---------------------------------
+
+def gpu_validated(B, D, xs, flags, t, flag, max_attempts=1):
+    k = xs[0].size
+    ins = [D.up(x) for x in xs]
+    fl = [torch.from_numpy(f.view(np.int32)).to("cuda:0") for f in flags]
+    out = D.filled(k, 0xFFFF)
+    at = torch.full((k // t,), -1, dtype=torch.int32, device="cuda:0")
+    B.pc_reduce_validated(ins, fl, out, k, t, flag, max_attempts, at)
+    return D.down(out, np.uint16), D.down(at, np.uint32)
+
+
+@pytest.mark.parametrize("n,t,tiles", [(1, 2048, 3), (3, 4096, 5), (5, 6144, 7), (8, 8192, 33),
+                                       (8, 2048, 1025)])
+def test_reduce_validated_shapes(B, D, orc, n, t, tiles):
+    case = synth.ValidatedCase("v", 81 + n, n, t * tiles, t, flag=0x1234, stale_frac=0.1)
+    xs, fl = case.payloads(), case.flags()
+    want_out, want_ok = orc.reduce_validated(xs, fl, t, case.flag)
+    got_out, got_at = gpu_validated(B, D, xs, fl, t, case.flag)
+    assert np.array_equal(got_at, want_ok)              # static inputs: attempt 1 or never
+    assert np.array_equal(got_out, want_out)
+
+
+def test_reduce_validated_decode_and_retry_bound(B, D, orc):
+    case = synth.C1V_VALIDATED_8K
+    xs, fl = case.payloads(), case.flags()
+    got_out, got_at = gpu_validated(B, D, xs, fl, case.elems_per_flag, case.flag)
+    assert list(got_at) == [1] and np.array_equal(got_out, orc.reduce(xs))
+    # A rank that never reaches the call: every attempt fails, the call ends.
+    stale = [f.copy() for f in fl]
+    stale[3][0] -= 1
+    got_out, got_at = gpu_validated(B, D, xs, stale, case.elems_per_flag, case.flag, max_attempts=64)
+    assert list(got_at) == [0] and np.all(got_out == 0xFFFF)
+
+
+def test_reduce_validated_flags_fold_and_wrap(B, D, orc):
+    n, t = 3, 2048
+    xs = [synth.uniform_bf16(90, 0, r, t) for r in range(n)]
+    comp = [np.array([6], np.uint32), np.array([8], np.uint32), np.array([7], np.uint32)]
+    got_out, got_at = gpu_validated(B, D, xs, comp, t, 7)
+    assert list(got_at) == [1] and np.array_equal(got_out, orc.reduce(xs))
+    top = [np.array([0xFFFFFFFF], np.uint32)] * n
+    got_out, got_at = gpu_validated(B, D, xs, top, t, 0xFFFFFFFF)
+    assert list(got_at) == [1]
+
+
+def test_reduce_validated_in_place(B, D, orc):
+    n, t = 4, 4096
+    xs = [synth.uniform_bf16(91, 0, r, 4 * t) for r in range(n)]
+    ins = [D.up(x) for x in xs]
+    fl = [torch.full((4,), 5, dtype=torch.int32, device="cuda:0") for _ in range(n)]
+    at = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    B.pc_reduce_validated(ins, fl, ins[1], 4 * t, t, 5, 1, at)
+    assert np.array_equal(D.down(ins[1], np.uint16), orc.reduce(xs))
