@@ -15,8 +15,10 @@
 // covers 1 KiB of consecutive bytes per rank.  All N*U loads of a lane are
 // issued before its first fold, which keeps N*U*16 bytes per lane in flight:
 // the gfx950 counterpart of sizing a copy pipeline to the bandwidth-delay
-// product (Purlin, Section 3.3, Equation (3)).  The tile count is far above
-// the 256 CUs for bandwidth-sized payloads, so every XCD streams.
+// product (Purlin, Section 3.3, Equation (3)).  Cache-resident payloads use
+// one workgroup per tile (k_reduce); payloads far beyond the last-level cache
+// use a persistent grid (k_reduce_persistent).  Three output modes cover the
+// oneshot reduce, twoshot phase 1 and the single-launch twoshot.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 
@@ -287,10 +289,6 @@ hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size
         default: return hipErrorInvalidValue;
     }
 }
-
-}  // namespace pcdp
-
-namespace pcdp {
 
 hipError_t launch_twoshot_fused(const void* const* src, int n, void* const* outs,
                                 size_t nchunks_slice, hipStream_t stream) {
