@@ -482,3 +482,62 @@ def test_reduce_validated_in_place(B, D, orc):
     at = torch.empty(4, dtype=torch.int32, device="cuda:0")
     B.pc_reduce_validated(ins, fl, ins[1], 4 * t, t, 5, 1, at)
     assert np.array_equal(D.down(ins[1], np.uint16), orc.reduce(xs))
+
+
+# ---- graph capture and concurrent streams ------------------------------------------------
+
+def test_graph_replays_match_oracle(B, D, orc):
+    """Calls captured once in a HIP graph and replayed several times, with the
+    inputs rewritten eagerly between replays: every replay must equal the
+    oracle on the inputs it saw (the library records only kernel launches)."""
+    n, k = 8, 8 * 4096
+    lines_k = 4096
+    ins = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
+    red = torch.empty(k, dtype=torch.int16, device="cuda:0")
+    outs = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
+    lines = [torch.empty(lines_k // 2, dtype=torch.int64, device="cuda:0") for _ in range(n)]
+    ll_out = torch.empty(lines_k, dtype=torch.int16, device="cuda:0")
+    ll_bm = torch.empty(lines_k // 128, dtype=torch.int64, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            B.pc_reduce(ins, red, k)
+            B.pc_twoshot_fused(ins, outs, k)
+            for r in range(n):
+                B.pc_pack_ll(ins[r], lines[r], lines_k, 9)
+            B.pc_consume_ll(lines, ll_out, lines_k, 9, ll_bm)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        xs = [synth.normal_bf16(1200 + rep, 0, r, k) for r in range(n)]
+        for t, x in zip(ins, xs):
+            t.copy_(D.up(x))                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = orc.reduce(xs)
+        assert np.array_equal(D.down(red, np.uint16), want), rep
+        for o in outs:
+            assert np.array_equal(D.down(o, np.uint16), want), rep
+        wo, wb = orc.consume_ll([orc.pack_ll(x[:lines_k], 9) for x in xs], lines_k, 9)
+        assert np.array_equal(D.down(ll_out, np.uint16), wo), rep
+        assert np.array_equal(D.down(ll_bm, np.uint64), wb), rep
+
+
+def test_two_streams_disjoint_buffers(B, D, orc):
+    n, k = 4, 8 * 65536
+    xa = [synth.uniform_bf16(1300, 0, r, k) for r in range(n)]
+    xb = [synth.uniform_bf16(1301, 0, r, k) for r in range(n)]
+    ia, ib = [D.up(x) for x in xa], [D.up(x) for x in xb]
+    oa = D.filled(k, 0xFFFF)
+    ob = [D.filled(k, 0xFFFF) for _ in range(n)]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(20):
+        B.pc_reduce(ia, oa, k, stream=sa)
+        B.pc_twoshot_fused(ib, ob, k, stream=sb)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.down(oa, np.uint16), orc.reduce(xa))
+    want = orc.reduce(xb)
+    assert all(np.array_equal(D.down(o, np.uint16), want) for o in ob)
