@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
                     choices=["all", "headline", "c1", "c1v", "c2", "c2s", "c3", "c5", "sweep",
-                             "copy"],
+                             "sweep_cold", "copy"],
                     help="run one part only (profiling); 'copy' times a plain device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -119,6 +119,35 @@ class Dev:
         torch.cuda.synchronize()
         del g
         return a.elapsed_time(b) * 1000.0 / (calls * replays)
+
+
+def graph_us_cold(d, fn, flush, calls=128, replays=8):
+    """Like Dev.graph_us, but the caches are flushed (a 512 MiB read-modify-
+    write, outside the timed region) before each timed replay, and the caller
+    gives every captured call its own inputs."""
+    torch = d.torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                fn()
+    torch.cuda.synchronize()
+    g.replay()
+    total = 0.0
+    for _ in range(replays):
+        flush.add_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+    del g
+    return total * 1000.0 / (calls * replays)
 
 
 def timing(d, fn, steps, warmup):
@@ -407,6 +436,50 @@ def run_sweep(d, B, synth, oracle, args, out):
     out["latency_sweep"] = rows
 
 
+def run_sweep_cold(d, B, synth, oracle, args, out):
+    """Cold per-call latency: each of the 128 captured calls reads its own
+    region of a 1 GiB arena and the caches are flushed before each timed
+    replay, so no call finds its inputs in the 256 MiB last-level cache (on
+    the pages' systems, peers have just written the inputs)."""
+    torch = d.torch
+    flush = torch.zeros((512 << 20) // 4, dtype=torch.int32, device=d.dev)
+    arena_elems = (1 << 30) // 2
+    g = torch.Generator(device=d.dev)
+    g.manual_seed(99)
+    arena = torch.randint(-32768, 32768, (arena_elems,), dtype=torch.int32, device=d.dev,
+                          generator=g).to(torch.int16)
+    rows = []
+    for nbytes in synth.SWEEP_BYTES:
+        k = nbytes // 2
+        for kind, n in (("reduce", 8), ("twoshot_fused", 8)):
+            per_call = n * k
+            calls = 128
+            res = [torch.empty(k, dtype=torch.int16, device=d.dev) for _ in range(n)]
+            ptr = [0]
+
+            def fn():
+                base = (ptr[0] * per_call) % (arena_elems - per_call)
+                base -= base % 8
+                ptr[0] += 1
+                ins = [arena[base + r * k: base + (r + 1) * k] for r in range(n)]
+                if kind == "reduce":
+                    B.pc_reduce(ins, res[0], k)
+                else:
+                    B.pc_twoshot_fused(ins, res, k)
+            us = graph_us_cold(d, fn, flush, calls=calls, replays=8)
+            rows.append({"call": kind, "n": n, "bytes_per_rank": nbytes, "graph_us_cold": round(us, 3)})
+    # Parity of one cold call against the oracle.
+    if oracle is not None:
+        k = 4096
+        ins = [arena[(1 << 20) + r * k: (1 << 20) + (r + 1) * k] for r in range(8)]
+        res0 = torch.empty(k, dtype=torch.int16, device=d.dev)
+        B.pc_reduce(ins, res0, k)
+        xs = [d.down(t, np.uint16) for t in ins]
+        out["parity"]["sweep_cold"] = bool(np.array_equal(d.down(res0, np.uint16), oracle.reduce(xs)))
+    out["latency_sweep_cold"] = rows
+    del arena, flush
+
+
 def run_floor(d, out):
     torch = d.torch
     fn = lambda: torch.cuda._sleep(0)  # noqa: E731
@@ -450,7 +523,7 @@ def main():
     if args.only == "copy":
         run_copy(d, out, args.steps)
     for name, fn in (("c1", run_c1), ("c1v", run_c1v), ("c2", run_c2), ("c2s", run_c2s), ("c3", run_c3),
-                     ("c5", run_c5), ("sweep", run_sweep)):
+                     ("c5", run_c5), ("sweep", run_sweep), ("sweep_cold", run_sweep_cold)):
         if args.only in ("all", name):
             log("running", name)
             fn(d, B, synth, oracle, args, out)
