@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604016195,
+TRAFFIC = {"bytes": 604016309,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "7290097cc08dbb5b6606992b7aabecf27954aaec3c89442d65892b2596b1ad94"}
+           "sha256": "5f9162a37b78e9ed533e1cd368d6d6be9957fecb44f2cd77f4781ff42a2b04f2"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -546,6 +546,7 @@ def main():
                             "kernel": "pcdp::k_reduce_persistent<8, (pcdp::Out)0>"}
     if "cpu_baseline" in out:
         line["cpu_baseline"] = out.pop("cpu_baseline")
+    line["parity_ok"] = bool(out["parity"]) and all(out["parity"].values())
     line.update(out)
     print(json.dumps(line), flush=True)
 
