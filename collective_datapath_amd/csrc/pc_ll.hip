@@ -20,17 +20,20 @@
 
 namespace pcdp {
 
-constexpr int kLLBlock = 256;
-constexpr int kLLWaves = kLLBlock / kWave;
+// Launch shapes: W waves per workgroup, U 64-line groups (consume) or
+// 16-byte chunks (pack) per lane.  Payloads under 4 MiB per rank take one
+// group or chunk per lane, so a 128 KiB call still spreads over more
+// workgroups (the two-per-lane shape measured 0.5 us slower per call there).
 
 // ---- pack: 8 bf16 (16 bytes) in -> 4 lines (32 bytes) out -----------------------
-template <int U>
-__global__ __launch_bounds__(kLLBlock) void k_pack_ll(const u32x4* src, u32x4* dst, uint32_t seq,
-                                                       size_t nchunks) {
-    const size_t tile0 = (size_t)blockIdx.x * (kLLBlock * U);
+template <int W, int U>
+__global__ __launch_bounds__(W * kWave) void k_pack_ll(const u32x4* src, u32x4* dst, uint32_t seq,
+                                                        size_t nchunks) {
+    constexpr int kBlk = W * kWave;
+    const size_t tile0 = (size_t)blockIdx.x * (kBlk * U);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const size_t c = tile0 + u * kLLBlock + threadIdx.x;
+        const size_t c = tile0 + u * kBlk + threadIdx.x;
         if (c < nchunks) {
             const u32x4 v = src[c];
             u32x4 a, b;
@@ -48,13 +51,13 @@ __global__ __launch_bounds__(kLLBlock) void k_pack_ll(const u32x4* src, u32x4* d
 // group (bit l = line base + 64u + l), so no bit shuffling is needed.  Lines
 // that are ready are folded in rank order and stored; the rest are skipped,
 // leaving their output as it was.
-template <int N, int U>
-__global__ __launch_bounds__(kLLBlock) void k_consume_ll(Ptrs<const u32x2*> lines, uint32_t* out,
-                                                          uint64_t* bitmap, uint32_t seq,
-                                                          size_t nlines) {
+template <int N, int W, int U>
+__global__ __launch_bounds__(W * kWave) void k_consume_ll(Ptrs<const u32x2*> lines, uint32_t* out,
+                                                           uint64_t* bitmap, uint32_t seq,
+                                                           size_t nlines) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = threadIdx.x / kWave;
-    const size_t base = ((size_t)blockIdx.x * kLLWaves + wave) * (kWave * U);
+    const size_t base = ((size_t)blockIdx.x * W + wave) * (kWave * U);
     if (base >= nlines) return;  // whole wave past the end
     u32x2 l[U][N];
 #pragma unroll
@@ -85,25 +88,41 @@ __global__ __launch_bounds__(kLLBlock) void k_consume_ll(Ptrs<const u32x2*> line
     }
 }
 
+// Bytes per rank below which the one-wave shapes are used.
+constexpr size_t kSmallBytes = (size_t)4 << 20;
+
+template <int W, int U>
+static hipError_t go_pack(const u32x4* s, u32x4* d, uint32_t seq, size_t nchunks, hipStream_t stream) {
+    const size_t tile = (size_t)W * kWave * U;
+    dim3 grid((unsigned)((nchunks + tile - 1) / tile));
+    void* args[] = {&s, &d, &seq, &nchunks};
+    return hipLaunchKernel((const void*)&k_pack_ll<W, U>, grid, dim3(W * kWave), args, 0, stream);
+}
+
 hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t seq,
                           hipStream_t stream) {
-    constexpr int U = 2;
-    const size_t tile = (size_t)kLLBlock * U;
-    dim3 grid((unsigned)((nchunks + tile - 1) / tile));
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
-    void* args[] = {&s, &d, &seq, &nchunks};
-    return hipLaunchKernel((const void*)&k_pack_ll<U>, grid, dim3(kLLBlock), args, 0, stream);
+    if (nchunks * 16 < kSmallBytes) return go_pack<4, 1>(s, d, seq, nchunks, stream);
+    return go_pack<4, 2>(s, d, seq, nchunks, stream);
+}
+
+template <int N, int W, int U>
+static hipError_t go_consume_shape(Ptrs<const u32x2*> p, uint32_t* out, uint64_t* bitmap,
+                                   uint32_t seq, size_t nlines, hipStream_t stream) {
+    const size_t per_block = (size_t)W * kWave * U;
+    dim3 grid((unsigned)((nlines + per_block - 1) / per_block));
+    void* args[] = {&p, &out, &bitmap, &seq, &nlines};
+    return hipLaunchKernel((const void*)&k_consume_ll<N, W, U>, grid, dim3(W * kWave), args, 0,
+                           stream);
 }
 
 template <int N>
 static hipError_t go_consume(Ptrs<const u32x2*> p, uint32_t* out, uint64_t* bitmap, uint32_t seq,
                              size_t nlines, hipStream_t stream) {
-    constexpr int U = 2;
-    const size_t per_block = (size_t)kLLWaves * kWave * U;
-    dim3 grid((unsigned)((nlines + per_block - 1) / per_block));
-    void* args[] = {&p, &out, &bitmap, &seq, &nlines};
-    return hipLaunchKernel((const void*)&k_consume_ll<N, U>, grid, dim3(kLLBlock), args, 0, stream);
+    if (nlines * 4 < kSmallBytes)
+        return go_consume_shape<N, 4, 1>(p, out, bitmap, seq, nlines, stream);
+    return go_consume_shape<N, 4, 2>(p, out, bitmap, seq, nlines, stream);
 }
 
 hipError_t launch_consume_ll(const void* const* lines, int n, void* out, size_t nlines,

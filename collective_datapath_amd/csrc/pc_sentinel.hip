@@ -20,8 +20,8 @@
 
 namespace pcdp {
 
-constexpr int kSBlock = 256;
-constexpr int kSWaves = kSBlock / kWave;
+// Bytes per rank below which one pack or chunk per lane is used.
+constexpr size_t kSentinelSmallBytes = (size_t)4 << 20;
 constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // two sentinel elements
 
 // 1 if neither bf16 half of `w` is the sentinel.
@@ -37,13 +37,14 @@ __device__ __forceinline__ uint32_t sanitize(uint32_t w) {
 }
 
 // ---- publish: copy with substitution, 16 bytes per lane ---------------------------
-template <int U>
-__global__ __launch_bounds__(kSBlock) void k_publish_sentinel(const u32x4* src, u32x4* dst,
-                                                               size_t nchunks) {
-    const size_t tile0 = (size_t)blockIdx.x * (kSBlock * U);
+template <int W, int U>
+__global__ __launch_bounds__(W * kWave) void k_publish_sentinel(const u32x4* src, u32x4* dst,
+                                                                 size_t nchunks) {
+    constexpr int kBlk = W * kWave;
+    const size_t tile0 = (size_t)blockIdx.x * (kBlk * U);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const size_t c = tile0 + u * kSBlock + threadIdx.x;
+        const size_t c = tile0 + u * kBlk + threadIdx.x;
         if (c < nchunks) {
             u32x4 v = src[c];
 #pragma unroll
@@ -58,12 +59,12 @@ __global__ __launch_bounds__(kSBlock) void k_publish_sentinel(const u32x4* src, 
 // wave's ballot over "no rank holds the sentinel anywhere in the pack" is the
 // group's bitmap word.  A ready pack is folded in rank order, stored, and its
 // slots are re-armed with the sentinel; other packs are left as they are.
-template <int N, int U>
-__global__ __launch_bounds__(kSBlock) void k_consume_sentinel(Ptrs<u32x4*> slots, u32x4* out,
-                                                               uint64_t* bitmap, size_t npacks) {
+template <int N, int W, int U>
+__global__ __launch_bounds__(W * kWave) void k_consume_sentinel(Ptrs<u32x4*> slots, u32x4* out,
+                                                                 uint64_t* bitmap, size_t npacks) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = threadIdx.x / kWave;
-    const size_t base = ((size_t)blockIdx.x * kSWaves + wave) * (kWave * U);
+    const size_t base = ((size_t)blockIdx.x * W + wave) * (kWave * U);
     if (base >= npacks) return;  // whole wave past the end
     u32x4 v[U][N];
 #pragma unroll
@@ -93,25 +94,38 @@ __global__ __launch_bounds__(kSBlock) void k_consume_sentinel(Ptrs<u32x4*> slots
     }
 }
 
-hipError_t launch_publish_sentinel(const void* src, void* dst, size_t nchunks, hipStream_t stream) {
-    constexpr int U = 2;
-    const size_t tile = (size_t)kSBlock * U;
+template <int W, int U>
+static hipError_t go_publish(const u32x4* s, u32x4* d, size_t nchunks, hipStream_t stream) {
+    const size_t tile = (size_t)W * kWave * U;
     dim3 grid((unsigned)((nchunks + tile - 1) / tile));
+    void* args[] = {&s, &d, &nchunks};
+    return hipLaunchKernel((const void*)&k_publish_sentinel<W, U>, grid, dim3(W * kWave), args, 0,
+                           stream);
+}
+
+hipError_t launch_publish_sentinel(const void* src, void* dst, size_t nchunks, hipStream_t stream) {
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
-    void* args[] = {&s, &d, &nchunks};
-    return hipLaunchKernel((const void*)&k_publish_sentinel<U>, grid, dim3(kSBlock), args, 0, stream);
+    if (nchunks * 16 < kSentinelSmallBytes) return go_publish<4, 1>(s, d, nchunks, stream);
+    return go_publish<4, 2>(s, d, nchunks, stream);
+}
+
+template <int N, int W, int U>
+static hipError_t go_consume_sentinel_shape(Ptrs<u32x4*> p, u32x4* out, uint64_t* bitmap,
+                                            size_t npacks, hipStream_t stream) {
+    const size_t per_block = (size_t)W * kWave * U;
+    dim3 grid((unsigned)((npacks + per_block - 1) / per_block));
+    void* args[] = {&p, &out, &bitmap, &npacks};
+    return hipLaunchKernel((const void*)&k_consume_sentinel<N, W, U>, grid, dim3(W * kWave), args, 0,
+                           stream);
 }
 
 template <int N>
 static hipError_t go_consume_sentinel(Ptrs<u32x4*> p, u32x4* out, uint64_t* bitmap, size_t npacks,
                                       hipStream_t stream) {
-    constexpr int U = 1;
-    const size_t per_block = (size_t)kSWaves * kWave * U;
-    dim3 grid((unsigned)((npacks + per_block - 1) / per_block));
-    void* args[] = {&p, &out, &bitmap, &npacks};
-    return hipLaunchKernel((const void*)&k_consume_sentinel<N, U>, grid, dim3(kSBlock), args, 0,
-                           stream);
+    if (npacks * 16 < kSentinelSmallBytes)
+        return go_consume_sentinel_shape<N, 4, 1>(p, out, bitmap, npacks, stream);
+    return go_consume_sentinel_shape<N, 4, 1>(p, out, bitmap, npacks, stream);
 }
 
 hipError_t launch_consume_sentinel(void* const* slots, int n, void* out, size_t npacks,
