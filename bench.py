@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604016309,
+TRAFFIC = {"bytes": 604518097,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "5f9162a37b78e9ed533e1cd368d6d6be9957fecb44f2cd77f4781ff42a2b04f2"}
+           "sha256": "3e7b91dee959a9e6c3cd21086a2b3195372b8d2fba63bb3fd3f06f7aa36da261"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 

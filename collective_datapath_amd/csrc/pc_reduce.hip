@@ -85,45 +85,88 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
 // host to whole rounds of at most two workgroups per CU, and workgroup w takes
 // tiles w, w + grid, w + 2*grid, ...  Each tile is 16 KiB per rank, accessed
 // through tile-sized buffer resources (a ragged last tile needs no branch).
-// Every lane issues all 4*N non-temporal loads and folds its 4 chunks; the
-// workgroup then passes a barrier and issues its stores together, as
-// device-scope stores.  Keeping each workgroup's writes in one burst after its
-// reads, the two-per-CU persistent grid, and the store policy each measurably
-// raise HBM efficiency for this 8:1 read/write mix (see the design notes).
-// Grid tile g covers slice g / tiles_per_slice.
+// A workgroup takes its tiles in batches of up to kBatch: for each tile every
+// lane issues all 4*N non-temporal loads and folds its 4 chunks, keeping the
+// results in registers; after the batch the workgroup passes a barrier and
+// issues all of the batch's stores together, as device-scope stores.  DRAM
+// then sees long runs of reads and long runs of writes instead of a fine mix;
+// for this 8:1 read/write stream that, the two-per-CU persistent grid and the
+// store policy each measurably raise HBM efficiency (see the design notes).
+// Grid tile g covers slice g / tiles_per_slice.  The fan-out mode stores each
+// result N times; it batches one tile, which keeps it free of register spills.
 template <int N, Out kOut>
-__global__ __launch_bounds__(kBlock) void k_reduce_persistent(Ptrs<const u32x4*> src,
-                                                                Ptrs<u32x4*> dst, uint32_t nslice,
-                                                                uint32_t tiles_per_slice,
-                                                                uint32_t ntiles) {
+constexpr int batch_tiles() { return kOut == Out::kAll ? 1 : 8; }
+
+// Geometry of grid tile g: its slice, first chunk and valid bytes per rank.
+struct TileAt {
+    uint32_t s;
+    size_t first;
+    uint32_t bytes;
+};
+
+template <Out kOut>
+__device__ __forceinline__ TileAt tile_at(uint32_t g, uint32_t nslice, uint32_t tiles_per_slice,
+                                          uint32_t tile_chunks) {
+    const uint32_t s = kOut == Out::kOne ? 0u : g / tiles_per_slice;
+    const uint32_t tile0 = (g - s * tiles_per_slice) * tile_chunks;
+    const uint32_t left = nslice - tile0;
+    return {s, (size_t)s * nslice + tile0, (left < tile_chunks ? left : tile_chunks) * 16u};
+}
+
+// One batch: tiles g0, g0 + stride, ... (kBatch of them).  kAllValid: every
+// tile of the batch exists, so the loads of consecutive tiles are free to
+// overlap; otherwise each tile is guarded (a workgroup's last batch).
+template <int N, Out kOut, int kBatch, bool kAllValid>
+__device__ __forceinline__ void reduce_batch(const Ptrs<const u32x4*>& src, const Ptrs<u32x4*>& dst,
+                                             uint32_t nslice, uint32_t tiles_per_slice,
+                                             uint32_t ntiles, uint32_t g0, uint32_t stride) {
     constexpr int U = 4;
     constexpr uint32_t kTile = kBlock * U;
     const uint32_t t = threadIdx.x;
-    for (uint32_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
-        const uint32_t s = kOut == Out::kOne ? 0u : g / tiles_per_slice;
-        const uint32_t tile0 = (g - s * tiles_per_slice) * kTile;
-        const size_t first = (size_t)s * nslice + tile0;
-        const uint32_t left = nslice - tile0;
-        const uint32_t bytes = (left < kTile ? left : kTile) * 16u;
+    u32x4 o[kBatch][U];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const uint32_t g = g0 + j * stride;
+        if (!kAllValid && g >= ntiles) continue;  // uniform for the workgroup
+        const TileAt at = tile_at<kOut>(g, nslice, tiles_per_slice, kTile);
         u32x4 v[U][N];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, bytes);
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + at.first, at.bytes);
 #pragma unroll
             for (int u = 0; u < U; ++u) v[u][r] = load16_tile(rs, (u * kBlock + t) * 16u);
         }
-        u32x4 o[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) o[u] = fold_chunk<N>(v[u]);
-        __syncthreads();
+        for (int u = 0; u < U; ++u) o[j][u] = fold_chunk<N>(v[u]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const uint32_t g = g0 + j * stride;
+        if (!kAllValid && g >= ntiles) continue;
+        const TileAt at = tile_at<kOut>(g, nslice, tiles_per_slice, kTile);
         constexpr int kFan = kOut == Out::kAll ? N : 1;
 #pragma unroll
         for (int f = 0; f < kFan; ++f) {
-            const int d = kOut == Out::kAll ? f : (kOut == Out::kOwner ? (int)s : 0);
-            const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dst.p[d] + first, bytes);
+            const int d = kOut == Out::kAll ? f : (kOut == Out::kOwner ? (int)at.s : 0);
+            const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dst.p[d] + at.first, at.bytes);
 #pragma unroll
-            for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, o[u]);
+            for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, o[j][u]);
         }
+    }
+}
+
+template <int N, Out kOut>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
+void k_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                         uint32_t tiles_per_slice, uint32_t ntiles) {
+    constexpr int kBatch = batch_tiles<N, kOut>();
+    const uint32_t stride = gridDim.x;
+    for (uint32_t g0 = blockIdx.x; g0 < ntiles; g0 += stride * kBatch) {
+        if (g0 + (kBatch - 1) * stride < ntiles)
+            reduce_batch<N, kOut, kBatch, true>(src, dst, nslice, tiles_per_slice, ntiles, g0, stride);
+        else
+            reduce_batch<N, kOut, kBatch, false>(src, dst, nslice, tiles_per_slice, ntiles, g0, stride);
     }
 }
 
