@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604518097,
+TRAFFIC = {"bytes": 604518090,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "3e7b91dee959a9e6c3cd21086a2b3195372b8d2fba63bb3fd3f06f7aa36da261"}
+           "sha256": "b1860e0be1660057962ebefba4fc10cbe4b3175421a18c5639ee8ca41219bc0f"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -122,9 +122,10 @@ class Dev:
 
 
 def graph_us_cold(d, fn, flush, calls=128, replays=8):
-    """Like Dev.graph_us, but the caches are flushed (a 512 MiB read-modify-
-    write, outside the timed region) before each timed replay, and the caller
-    gives every captured call its own inputs."""
+    """Like Dev.graph_us, but the caches are flushed before each timed replay
+    (a 512 MiB read-only pass, outside the timed region, which leaves them
+    holding clean unrelated lines), and the caller gives every captured call
+    its own inputs."""
     torch = d.torch
     fn()
     torch.cuda.synchronize()
@@ -139,7 +140,7 @@ def graph_us_cold(d, fn, flush, calls=128, replays=8):
     g.replay()
     total = 0.0
     for _ in range(replays):
-        flush.add_(1)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         g.replay()
@@ -438,9 +439,9 @@ def run_sweep(d, B, synth, oracle, args, out):
 
 def run_sweep_cold(d, B, synth, oracle, args, out):
     """Cold per-call latency: each of the 128 captured calls reads its own
-    region of a 1 GiB arena and the caches are flushed before each timed
-    replay, so no call finds its inputs in the 256 MiB last-level cache (on
-    the pages' systems, peers have just written the inputs)."""
+    region of a 1 GiB arena and the caches are flushed (read-only) before
+    each timed replay, so no call finds its inputs in the 256 MiB last-level
+    cache (on the pages' systems, peers have just written the inputs)."""
     torch = d.torch
     flush = torch.zeros((512 << 20) // 4, dtype=torch.int32, device=d.dev)
     arena_elems = (1 << 30) // 2

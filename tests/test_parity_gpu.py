@@ -78,6 +78,7 @@ def test_reduce_every_n_ragged_with_order(B, D, orc, n):
 @pytest.mark.parametrize("n,chunks", [
     (3, 262144 + 1234),           # mid-size shape: 4 MiB per rank and a tail
     (2, 4718592 + 77),            # streaming shape: 72 MiB per rank and a tail
+    (8, 524288 + 13),             # 8 MiB per rank: persistent kernel from a 64 MiB working set
     (8, 256 * 2 * 3 + 1),         # one chunk past whole tiles
     (4, 1),                       # a single chunk
 ])
