@@ -2,8 +2,12 @@
 
 Argument marshalling only: device buffers are torch tensors (or raw device
 addresses as ints), host pointer arrays are built here, and every call goes
-straight to the HIP library, which does all the work.  There is no fallback:
-if the built library is missing, importing this module fails.
+straight to the HIP library, which does all the work.  Tensors are checked
+to be on the current GPU, contiguous and large enough for the call, so a
+wrong tensor raises ValueError here rather than faulting on the device; the
+library itself validates everything else (alignment, sizes, overlaps).
+There is no fallback: if the built library is missing, importing this
+module fails.
 """
 from __future__ import annotations
 
@@ -87,16 +91,29 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-def _addr(b: Optional[Buffer]) -> int:
+def _addr(b: Optional[Buffer], nbytes: int = 0, what: str = "buffer") -> int:
+    """Device address of `b`.  A tensor must live on the current GPU, be
+    contiguous and hold at least `nbytes` bytes (what the call will touch);
+    anything else raises here instead of faulting on the device.  Raw int
+    addresses are passed through unchecked."""
     if b is None:
         return 0
     if isinstance(b, int):
         return b
+    if nbytes:
+        if not b.is_cuda or b.device.index != torch.cuda.current_device():
+            raise ValueError(f"{what} must be a tensor on the current GPU (got {b.device})")
+        if not b.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+        have = b.numel() * b.element_size()
+        if have < nbytes:
+            raise ValueError(f"{what} holds {have} bytes; the call needs {nbytes}")
     return b.data_ptr()
 
 
-def _addrs(bs: Sequence[Buffer]):
-    return (ctypes.c_void_p * max(len(bs), 1))(*[_addr(b) for b in bs])
+def _addrs(bs: Sequence[Buffer], nbytes: int = 0, what: str = "buffer"):
+    return (ctypes.c_void_p * max(len(bs), 1))(
+        *[_addr(b, nbytes, f"{what}[{i}]") for i, b in enumerate(bs)])
 
 
 def _stream(stream) -> int:
@@ -127,21 +144,21 @@ def pc_reduce(inputs: Sequence[Buffer], out: Buffer, k: int, order: Optional[Seq
     if order is not None and len(order) != len(inputs):
         raise ValueError("order must list every rank exactly once")
     ordp = (ctypes.c_int32 * len(order))(*order) if order is not None else None
-    st = _lib.pc_reduce(_addrs(inputs), len(inputs), _addr(out), k,
+    st = _lib.pc_reduce(_addrs(inputs, 2 * k, "inputs"), len(inputs), _addr(out, 2 * k, "out"), k,
                         ctypes.cast(ordp, ctypes.c_void_p) if ordp is not None else None,
                         _stream(stream))
     return _call("pc_reduce", st, check)
 
 
 def pc_pack_ll(src: Buffer, dst: Buffer, k: int, seq: int, stream=None, check: bool = True) -> int:
-    st = _lib.pc_pack_ll(_addr(src), _addr(dst), k, seq, _stream(stream))
+    st = _lib.pc_pack_ll(_addr(src, 2 * k, "src"), _addr(dst, 4 * k, "dst"), k, seq, _stream(stream))
     return _call("pc_pack_ll", st, check)
 
 
 def pc_consume_ll(lines: Sequence[Buffer], out: Buffer, k: int, seq: int, ready_bitmap: Buffer,
                   stream=None, check: bool = True) -> int:
-    st = _lib.pc_consume_ll(_addrs(lines), len(lines), _addr(out), k, seq, _addr(ready_bitmap),
-                            _stream(stream))
+    st = _lib.pc_consume_ll(_addrs(lines, 4 * k, "lines"), len(lines), _addr(out, 2 * k, "out"), k,
+                            seq, _addr(ready_bitmap, k // 128 * 8, "ready_bitmap"), _stream(stream))
     return _call("pc_consume_ll", st, check)
 
 
@@ -149,7 +166,8 @@ def pc_twoshot(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=
                check: bool = True) -> int:
     if len(outs) != len(inputs):
         raise ValueError("pc_twoshot needs one output per input")
-    st = _lib.pc_twoshot(_addrs(inputs), len(inputs), _addrs(outs), k, _stream(stream))
+    st = _lib.pc_twoshot(_addrs(inputs, 2 * k, "inputs"), len(inputs), _addrs(outs, 2 * k, "outs"),
+                         k, _stream(stream))
     return _call("pc_twoshot", st, check)
 
 
@@ -157,26 +175,31 @@ def pc_twoshot_fused(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, s
                      check: bool = True) -> int:
     if len(outs) != len(inputs):
         raise ValueError("pc_twoshot_fused needs one output per input")
-    st = _lib.pc_twoshot_fused(_addrs(inputs), len(inputs), _addrs(outs), k, _stream(stream))
+    st = _lib.pc_twoshot_fused(_addrs(inputs, 2 * k, "inputs"), len(inputs),
+                               _addrs(outs, 2 * k, "outs"), k, _stream(stream))
     return _call("pc_twoshot_fused", st, check)
 
 
 def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, seq: int,
                       ready_bitmap: Buffer, stream=None, check: bool = True) -> int:
-    st = _lib.pc_allgather_copy(_addrs(shards), len(shards), _addr(out), shard_bytes, seq,
-                                _addr(ready_bitmap), _stream(stream))
+    blocks = shard_bytes // PC_BLOCK_PAYLOAD_BYTES
+    st = _lib.pc_allgather_copy(_addrs(shards, blocks * PC_BLOCK_RECORD_BYTES, "shards"), len(shards),
+                                _addr(out, len(shards) * shard_bytes, "out"), shard_bytes, seq,
+                                _addr(ready_bitmap, len(shards) * blocks // 64 * 8, "ready_bitmap"),
+                                _stream(stream))
     return _call("pc_allgather_copy", st, check)
 
 
 def pc_publish_sentinel(src: Buffer, slot: Buffer, k: int, stream=None, check: bool = True) -> int:
-    st = _lib.pc_publish_sentinel(_addr(src), _addr(slot), k, _stream(stream))
+    st = _lib.pc_publish_sentinel(_addr(src, 2 * k, "src"), _addr(slot, 2 * k, "slot"), k,
+                                  _stream(stream))
     return _call("pc_publish_sentinel", st, check)
 
 
 def pc_consume_sentinel(slots: Sequence[Buffer], out: Buffer, k: int, ready_bitmap: Buffer,
                         stream=None, check: bool = True) -> int:
-    st = _lib.pc_consume_sentinel(_addrs(slots), len(slots), _addr(out), k, _addr(ready_bitmap),
-                                  _stream(stream))
+    st = _lib.pc_consume_sentinel(_addrs(slots, 2 * k, "slots"), len(slots), _addr(out, 2 * k, "out"),
+                                  k, _addr(ready_bitmap, k // 512 * 8, "ready_bitmap"), _stream(stream))
     return _call("pc_consume_sentinel", st, check)
 
 
@@ -185,7 +208,9 @@ def pc_reduce_validated(inputs: Sequence[Buffer], flags: Sequence[Buffer], out: 
                         stream=None, check: bool = True) -> int:
     if len(flags) != len(inputs):
         raise ValueError("pc_reduce_validated needs one flag buffer per input")
-    st = _lib.pc_reduce_validated(_addrs(inputs), _addrs(flags), len(inputs), _addr(out), k,
-                                  elems_per_flag, flag & 0xFFFFFFFF, max_attempts, _addr(attempts),
+    tiles = k // elems_per_flag if elems_per_flag else 0
+    st = _lib.pc_reduce_validated(_addrs(inputs, 2 * k, "inputs"), _addrs(flags, 4 * tiles, "flags"),
+                                  len(inputs), _addr(out, 2 * k, "out"), k, elems_per_flag,
+                                  flag & 0xFFFFFFFF, max_attempts, _addr(attempts, 4 * tiles, "attempts"),
                                   _stream(stream))
     return _call("pc_reduce_validated", st, check)

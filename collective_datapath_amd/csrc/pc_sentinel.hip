@@ -20,7 +20,7 @@
 
 namespace pcdp {
 
-// Bytes per rank below which one pack or chunk per lane is used.
+// Bytes per rank below which the publisher takes one chunk per lane.
 constexpr size_t kSentinelSmallBytes = (size_t)4 << 20;
 constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // two sentinel elements
 
@@ -120,11 +120,11 @@ static hipError_t go_consume_sentinel_shape(Ptrs<u32x4*> p, u32x4* out, uint64_t
                            stream);
 }
 
+// The consumer keeps one 64-pack group per lane at every size: a second group
+// per lane would hold 2*N 16-byte packs in registers for the re-arm pass.
 template <int N>
 static hipError_t go_consume_sentinel(Ptrs<u32x4*> p, u32x4* out, uint64_t* bitmap, size_t npacks,
                                       hipStream_t stream) {
-    if (npacks * 16 < kSentinelSmallBytes)
-        return go_consume_sentinel_shape<N, 4, 1>(p, out, bitmap, npacks, stream);
     return go_consume_sentinel_shape<N, 4, 1>(p, out, bitmap, npacks, stream);
 }
 

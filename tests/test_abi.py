@@ -191,3 +191,12 @@ FL = A + 2048 * MB
 ])
 def test_reduce_validated_validation(args, want):
     assert B.pc_reduce_validated(stream=0, check=False, **args) == want
+
+
+def test_binding_rejects_host_and_short_tensors():
+    import torch
+    cpu = torch.zeros(64, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        B.pc_reduce([cpu, cpu], cpu, 64, stream=0)
+    with pytest.raises(ValueError):
+        B.pc_publish_sentinel(cpu, cpu, 64, stream=0)

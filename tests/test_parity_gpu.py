@@ -542,3 +542,18 @@ def test_two_streams_disjoint_buffers(B, D, orc):
     assert np.array_equal(D.down(oa, np.uint16), orc.reduce(xa))
     want = orc.reduce(xb)
     assert all(np.array_equal(D.down(o, np.uint16), want) for o in ob)
+
+
+def test_binding_rejects_bad_tensors_before_launch(B, D):
+    k = 4096
+    x = D.up(synth.uniform_bf16(1310, 0, 0, k))
+    out = D.filled(k, 0xFFFF)
+    wide = torch.zeros(2 * k, dtype=torch.int16, device="cuda")
+    with pytest.raises(ValueError, match="contiguous"):
+        B.pc_reduce([wide[::2], x], out, k)
+    with pytest.raises(ValueError, match="bytes"):
+        B.pc_reduce([x, x], out[: k // 2], k)
+    with pytest.raises(ValueError, match="GPU"):
+        B.pc_reduce([x, x.cpu()], out, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.down(out, np.uint16), np.full(k, 0xFFFF, np.uint16))
