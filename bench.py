@@ -376,9 +376,14 @@ def run_c3(d, B, synth, oracle, args, out):
         one = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
         B.pc_reduce(ins, one, case.k)
         onev = d.down(one, np.uint16)
-    # Two launches (slice reduce, then copy-out) and the single-launch form.
+    # Two launches (slice reduce, then copy-out), the single-launch form, and
+    # the single launch whose phases are linked per tile by epoch flags.
+    ws = d.torch.zeros(B.pc_twoshot_linked_workspace_bytes(case.n, case.k) // 4,
+                       dtype=d.torch.int32, device=d.dev)
+    linked = lambda i, o, k: B.pc_twoshot_linked(i, o, k, ws)  # noqa: E731
     for name, fn, nbytes in (("twoshot_1m", B.pc_twoshot, 2 * case.k * (2 * case.n + 1)),
-                             ("twoshot_fused_1m", B.pc_twoshot_fused, 2 * case.k * 2 * case.n)):
+                             ("twoshot_fused_1m", B.pc_twoshot_fused, 2 * case.k * 2 * case.n),
+                             ("twoshot_linked_1m", linked, 2 * case.k * (2 * case.n + 1))):
         outs = [d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev) for _ in xs]
         t = timing(d, lambda: fn(ins, outs, case.k), 1000, 50)
         t.update(workload=case.name, bytes_per_call=nbytes,
@@ -387,6 +392,7 @@ def run_c3(d, B, synth, oracle, args, out):
         if oracle is not None:
             out["parity"][name] = bool(all(np.array_equal(d.down(o, np.uint16), w) and
                                            np.array_equal(w, onev) for o, w in zip(outs, want)))
+    out["configs"]["twoshot_linked_1m"]["waits_abandoned"] = int(ws[B.PC_LINKED_STATUS_WORD])
 
 
 def run_c5(d, B, synth, oracle, args, out):
@@ -411,7 +417,8 @@ def run_sweep(d, B, synth, oracle, args, out):
     rows = []
     for nbytes in synth.SWEEP_BYTES:
         k = nbytes // 2
-        for kind, n in (("reduce", 4), ("reduce", 8), ("twoshot", 8), ("twoshot_fused", 8)):
+        for kind, n in (("reduce", 4), ("reduce", 8), ("twoshot", 8), ("twoshot_fused", 8),
+                        ("twoshot_linked", 8)):
             xs = [synth.uniform_bf16(20, 0, r, k) for r in range(n)]
             ins = [d.up(x) for x in xs]
             if kind == "reduce":
@@ -422,10 +429,16 @@ def run_sweep(d, B, synth, oracle, args, out):
                 outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
                 fn = lambda: B.pc_twoshot(ins, outs, k)  # noqa: E731
                 moved = (2 * n + 1) * nbytes
-            else:
+            elif kind == "twoshot_fused":
                 outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
                 fn = lambda: B.pc_twoshot_fused(ins, outs, k)  # noqa: E731
                 moved = 2 * n * nbytes
+            else:
+                outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
+                ws = d.torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4,
+                                   dtype=d.torch.int32, device=d.dev)
+                fn = lambda: B.pc_twoshot_linked(ins, outs, k, ws)  # noqa: E731
+                moved = (2 * n + 1) * nbytes
             t = timing(d, fn, 500, 50)
             row = {"call": kind, "n": n, "bytes_per_rank": nbytes, **t,
                    "gbs_cache_resident": round(gbs(moved, t["graph_us"]), 1)}

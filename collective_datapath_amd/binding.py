@@ -26,9 +26,11 @@ PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
 EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
+           "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated", "pc_strerror", "pc_abi_version")
 PC_MAX_ATTEMPTS = 65536
+PC_LINKED_GROUPS = 256
+PC_LINKED_STATUS_WORD = 256
 PC_SENTINEL = 0xFFFF
 
 if not os.path.exists(LIB_PATH):
@@ -66,12 +68,15 @@ _lib.pc_pack_ll.argtypes = [_P, _P, _S, ctypes.c_uint32, _P]
 _lib.pc_consume_ll.argtypes = [_P, _I, _P, _S, ctypes.c_uint32, _P, _P]
 _lib.pc_twoshot.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_twoshot_fused.argtypes = [_P, _I, _P, _S, _P]
+_lib.pc_twoshot_linked.argtypes = [_P, _I, _P, _S, _P, _S, _P]
+_lib.pc_twoshot_linked_workspace_bytes.argtypes = [_I, _S]
+_lib.pc_twoshot_linked_workspace_bytes.restype = _S
 _lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
 _lib.pc_publish_sentinel.argtypes = [_P, _P, _S, _P]
 _lib.pc_reduce_validated.argtypes = [_P, _P, _I, _P, _S, _S, ctypes.c_uint32, ctypes.c_uint32, _P, _P]
 _lib.pc_consume_sentinel.argtypes = [_P, _I, _P, _S, _P, _P]
 for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
+           "pc_twoshot_linked", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated"):
     getattr(_lib, _f).restype = _I
 _lib.pc_strerror.argtypes = [_I]
@@ -178,6 +183,29 @@ def pc_twoshot_fused(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, s
     st = _lib.pc_twoshot_fused(_addrs(inputs, 2 * k, "inputs"), len(inputs),
                                _addrs(outs, 2 * k, "outs"), k, _stream(stream))
     return _call("pc_twoshot_fused", st, check)
+
+
+def pc_twoshot_linked_workspace_bytes(n: int, k: int) -> int:
+    return _lib.pc_twoshot_linked_workspace_bytes(n, k)
+
+
+def pc_twoshot_linked(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, workspace: Buffer,
+                      workspace_bytes: Optional[int] = None, stream=None, check: bool = True) -> int:
+    """`workspace`: zero-filled before its first use, then reused unchanged
+    across calls.  `workspace_bytes` defaults to the size of a workspace
+    tensor and must be given for a raw address."""
+    if len(outs) != len(inputs):
+        raise ValueError("pc_twoshot_linked needs one output per input")
+    if workspace_bytes is None:
+        if isinstance(workspace, int):
+            raise ValueError("workspace_bytes is needed with a raw workspace address")
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    need = pc_twoshot_linked_workspace_bytes(len(inputs), k) if k else 0
+    st = _lib.pc_twoshot_linked(_addrs(inputs, 2 * k, "inputs"), len(inputs),
+                                _addrs(outs, 2 * k, "outs"), k,
+                                _addr(workspace, min(need, workspace_bytes), "workspace"),
+                                workspace_bytes, _stream(stream))
+    return _call("pc_twoshot_linked", st, check)
 
 
 def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, seq: int,

@@ -1,0 +1,235 @@
+// pc_linked.hip -- single-launch twoshot whose two phases are linked per tile
+// by epoch-stamped readiness flags, with the epoch kept on the device.
+//
+// "flash-comm: Self-Synchronizing Collective Communication for LLM
+// Decoding", Section 4.3 (sharded two-hop: readiness checks join the
+// reduce-scatter and the result distribution tile by tile, so a finished
+// owner tile is distributed while other tiles are still being reduced) and
+// Section 4.2 (each thread group derives its state from a call counter kept
+// on the device, because launch arguments are frozen once a graph is
+// captured; one family runs on one fixed grid so that the counters stay in
+// step; every rank issues the same sequence of calls).  "Purlin: Separating
+// Orchestration from the Datapath of Collectives", Section 4.2 (every
+// thread block keeps a persistent epoch that it advances after each call,
+// and that epoch is the value a producer writes to signal readiness) and
+// Section 3.2 (the consumer waits on the notification, then moves the data).
+//
+// Workspace (caller-owned, zero before its first use, uint32 words):
+//   [0, G)          call counter of workgroup w (G = kLinkGroups)
+//   [G]             number of tiles whose wait gave up (sticky)
+//   [G + 64, ...)   flag of tile t: the epoch of the call that last
+//                   finished reducing it
+// Workgroup w runs call number ctr[w] + 1 as its epoch and stores it back
+// when it is done.  Every call launches all G workgroups, so all counters
+// agree and a stale flag (an earlier epoch, or zero) never equals the
+// current one; no flag has to be cleared between calls, and a graph replay
+// advances the epoch by itself.
+//
+// Tile t = (slice s, tile j of the slice) covers up to 256*U chunks of 16
+// bytes of slice s.  Phase 1: workgroup t mod G folds tile t from the n
+// inputs into outs[s] (the owner's copy); once all of its tiles are stored
+// it publishes their flags behind one release at agent scope.  Phase 2:
+// workgroup (t + G/2) mod G waits for the flags of its tiles, acquires once
+// at agent scope, reads each owner tile and writes it to every other
+// outs[r].  Every workgroup finishes phase 1 before it waits on any flag,
+// and the grid is small enough to be resident at once (checked before
+// launch), so every awaited flag is eventually published.  The wait is
+// still bounded: a workgroup that gives up adds the number of its tiles to
+// the status word and skips them, so the kernel always ends.
+#include "pc_device.hpp"
+#include "pc_launch.hpp"
+
+#include <atomic>
+
+namespace pcdp {
+
+constexpr int kLinkBlock = 256;
+constexpr uint32_t kMaxPolls = 1u << 20;
+
+template <int kPolicy>
+__device__ __forceinline__ u32x4 load16_policy(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kPolicy));
+}
+
+// Chunks of tile j of a slice of `slice_chunks` chunks, as a byte count.
+template <uint32_t kTile>
+__device__ __forceinline__ uint32_t tile_bytes(size_t slice_chunks, size_t j) {
+    const size_t left = slice_chunks - j * kTile;
+    return (uint32_t)(left < kTile ? left : kTile) * 16u;
+}
+
+template <int N, int U, bool kStream>
+__global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*> src,
+                                                                Ptrs<u32x4*> outs, uint32_t* ws,
+                                                                size_t slice_chunks,
+                                                                size_t tiles_per_slice) {
+    constexpr uint32_t kTile = kLinkBlock * U;  // chunks per tile
+    constexpr int kLoadPolicy = kStream ? kPolicyNonTemporal : 0;
+    __shared__ uint32_t shared_epoch, ready;
+    const uint32_t w = blockIdx.x, tid = threadIdx.x;
+    uint32_t* const ctr = ws;
+    uint32_t* const status = ws + kLinkGroups;
+    uint32_t* const flags = ws + kLinkGroups + kLinkHeaderWords;
+
+    if (tid == 0) shared_epoch = ctr[w] + 1u;
+    __syncthreads();
+    const uint32_t epoch = shared_epoch;
+    const size_t ntiles = (size_t)N * tiles_per_slice;
+
+    // ---- phase 1: fold this workgroup's owner tiles, then publish them -----------
+    // One release per workgroup: after the barrier, lane 0's agent-scope fence
+    // orders every wave's stores before the flags (the barrier-then-lane-0
+    // pattern of a grid-wide barrier).  Fences are few on purpose: each one
+    // writes back or invalidates a whole L2 and they queue up per XCD.
+    if (w < ntiles) {
+        for (size_t t = w; t < ntiles; t += kLinkGroups) {
+            const size_t s = t / tiles_per_slice, j = t % tiles_per_slice;
+            const size_t c0 = s * slice_chunks + j * kTile;
+            const uint32_t bytes = tile_bytes<kTile>(slice_chunks, j);
+            u32x4 v[U][N];
+#pragma unroll
+            for (int r = 0; r < N; ++r) {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + c0, bytes);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[u][r] = load16_policy<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
+            }
+            const __amdgpu_buffer_rsrc_t ro = tile_rsrc(outs.p[s] + c0, bytes);
+#pragma unroll
+            for (int u = 0; u < U; ++u) store16_tile(ro, (u * kLinkBlock + tid) * 16u, fold_chunk<N>(v[u]));
+        }
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            for (size_t t = w; t < ntiles; t += kLinkGroups)
+                __hip_atomic_store(flags + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // ---- phase 2: wait for the flags of this workgroup's tiles, copy them out -----
+    // Lane 0 waits for every flag in turn (bounded), acquires once, and the
+    // barrier hands the go-ahead to the other waves.  A workgroup that gives
+    // up copies none of its tiles and adds their number to the status word.
+    const size_t first = (w + kLinkGroups / 2) % kLinkGroups;
+    if (first < ntiles) {
+        if (tid == 0) {
+            bool ok = true;
+            uint32_t mine = 0;
+            for (size_t t = first; t < ntiles; t += kLinkGroups) {
+                ++mine;
+                uint32_t polls = 0;
+                while (ok && __hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+                    if (++polls >= kMaxPolls) ok = false;
+                    else __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            else __hip_atomic_fetch_add(status, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ready = ok;
+        }
+        __syncthreads();
+        if (ready) {
+            for (size_t t = first; t < ntiles; t += kLinkGroups) {
+                const size_t s = t / tiles_per_slice, j = t % tiles_per_slice;
+                const size_t c0 = s * slice_chunks + j * kTile;
+                const uint32_t bytes = tile_bytes<kTile>(slice_chunks, j);
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(outs.p[s] + c0, bytes);
+                u32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = load16_policy<0>(rs, (u * kLinkBlock + tid) * 16u);
+                // The owner's own range gets a zero-length resource, so its
+                // stores are dropped without a branch.
+#pragma unroll
+                for (int r = 0; r < N; ++r) {
+                    const __amdgpu_buffer_rsrc_t rd = tile_rsrc(outs.p[r] + c0, (size_t)r == s ? 0u : bytes);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) store16_tile(rd, (u * kLinkBlock + tid) * 16u, v[u]);
+                }
+            }
+        }
+    }
+    if (tid == 0) ctr[w] = epoch;
+}
+
+// Chunks per lane per tile, from a sweep at 8 ranks: one below 512 KiB per
+// rank (the most tiles in flight), two below 4 MiB (half the tiles, and
+// half the fences, at 1 MiB), four above.
+static int linked_unroll(size_t nchunks_slice, int n) {
+    const size_t per_rank = nchunks_slice * (size_t)n * 16;
+    return per_rank < ((size_t)512 << 10) ? 1 : per_rank < ((size_t)4 << 20) ? 2 : 4;
+}
+
+size_t linked_tiles(int n, size_t nchunks_slice) {
+    const size_t tile = (size_t)kLinkBlock * linked_unroll(nchunks_slice, n);
+    return (size_t)n * ((nchunks_slice + tile - 1) / tile);
+}
+
+// Workgroups of `kernel` that fit on the device at once, cached per device
+// and kernel (the answer does not change while the process runs).
+static hipError_t resident_capacity(const void* kernel, int* capacity) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kLinkBlock, 0);
+    if (e != hipSuccess) return e;
+    *capacity = cus * per_cu;
+    return hipSuccess;
+}
+
+template <int N, int U, bool kStream>
+static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint32_t* ws, size_t slice_chunks,
+                            hipStream_t stream) {
+    const void* kernel = (const void*)&k_twoshot_linked<N, U, kStream>;
+    // 0 = not yet known, else capacity + 1, per device.
+    static std::atomic<int> known[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cap = dev >= 0 && dev < 64 ? known[dev].load(std::memory_order_relaxed) - 1 : -1;
+    if (cap < 0) {
+        e = resident_capacity(kernel, &cap);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) known[dev].store(cap + 1, std::memory_order_relaxed);
+    }
+    if (cap < (int)kLinkGroups) return hipErrorCooperativeLaunchTooLarge;
+    const size_t tile = (size_t)kLinkBlock * U;
+    size_t tiles_per_slice = (slice_chunks + tile - 1) / tile;
+    void* args[] = {&s, &o, &ws, &slice_chunks, &tiles_per_slice};
+    return hipLaunchKernel(kernel, dim3(kLinkGroups), dim3(kLinkBlock), args, 0, stream);
+}
+
+template <int N>
+static hipError_t go_linked_n(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint32_t* ws, size_t slice_chunks,
+                              hipStream_t stream) {
+    switch (linked_unroll(slice_chunks, N)) {
+        case 1: return go_linked<N, 1, false>(s, o, ws, slice_chunks, stream);
+        case 2: return go_linked<N, 2, false>(s, o, ws, slice_chunks, stream);
+        default: return go_linked<N, 4, true>(s, o, ws, slice_chunks, stream);
+    }
+}
+
+hipError_t launch_twoshot_linked(const void* const* src, int n, void* const* outs,
+                                 size_t nchunks_slice, void* workspace, hipStream_t stream) {
+    Ptrs<const u32x4*> s;
+    Ptrs<u32x4*> o;
+    for (int r = 0; r < kMaxRanks; ++r) {
+        s.p[r] = r < n ? static_cast<const u32x4*>(src[r]) : nullptr;
+        o.p[r] = r < n ? static_cast<u32x4*>(outs[r]) : nullptr;
+    }
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    switch (n) {
+        case 1: return go_linked_n<1>(s, o, ws, nchunks_slice, stream);
+        case 2: return go_linked_n<2>(s, o, ws, nchunks_slice, stream);
+        case 3: return go_linked_n<3>(s, o, ws, nchunks_slice, stream);
+        case 4: return go_linked_n<4>(s, o, ws, nchunks_slice, stream);
+        case 5: return go_linked_n<5>(s, o, ws, nchunks_slice, stream);
+        case 6: return go_linked_n<6>(s, o, ws, nchunks_slice, stream);
+        case 7: return go_linked_n<7>(s, o, ws, nchunks_slice, stream);
+        case 8: return go_linked_n<8>(s, o, ws, nchunks_slice, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pcdp

@@ -61,11 +61,12 @@ enum {
                           /* order not a permutation, seq == 0, overlapping  */
                           /* buffers, size above the maximum                 */
     PC_EALIGN = -2,       /* a device pointer or a size is misaligned        */
-    PC_EUNSUPPORTED = -3, /* reserved                                        */
+    PC_EUNSUPPORTED = -3, /* the device cannot run the call (pc_twoshot_linked: */
+                          /* its fixed grid does not fit on the GPU at once)  */
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 4
+#define PC_ABI_VERSION 5
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -167,6 +168,49 @@ PC_API pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* cons
  */
 PC_API pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t* const* outs,
                                   size_t k, void* stream);
+
+/*
+ * pc_twoshot_linked -- twoshot in one launch, its two phases linked tile by
+ * tile through epoch-stamped readiness flags, the epoch kept on the device.
+ * Source: flash-comm, Section 4.3 (sharded two-hop: readiness checks join the
+ * slice reduction and the result distribution per block) and Section 4.2
+ * (state derived from a call counter kept on the device, so a captured graph
+ * can be replayed; one fixed grid per family; every rank issues the same
+ * call sequence); Purlin, Section 4.2 (a persistent per-block epoch advanced
+ * after each call is the value that signals readiness).
+ * Same inputs, outs, k, aliasing rules and result as pc_twoshot, bit for bit.
+ * The tiles of slice s are folded into outs[s] by one set of workgroups; each
+ * tile's flag is then set to the call's epoch, and other workgroups wait for
+ * that flag and copy the tile from outs[s] into every other outs[r].
+ *   workspace : device, 16-byte aligned, at least
+ *               pc_twoshot_linked_workspace_bytes(n, k) bytes, owned by the
+ *               caller.  It must be zero-filled before its first use and then
+ *               left to the library: it carries one call counter per
+ *               workgroup of a fixed grid of PC_LINKED_GROUPS workgroups, so
+ *               successive calls (and graph replays) need no host-side epoch
+ *               and no clearing.  A workspace serves any n and k it is large
+ *               enough for.  Two calls that may run at the same time (other
+ *               streams) need separate workspaces; it must not overlap any
+ *               input or output.
+ *   workspace[PC_LINKED_STATUS_WORD] : the number of tiles, summed over all
+ *               calls, whose wait for a flag was abandoned after a bounded
+ *               number of polls (their outputs are then incomplete).  It
+ *               stays 0 while the grid is resident, which is checked before
+ *               launch.
+ * Errors: PC_EINVAL (also: NULL workspace, workspace_bytes too small,
+ * workspace overlapping a buffer), PC_EALIGN, PC_EUNSUPPORTED (the device
+ * cannot hold PC_LINKED_GROUPS of these workgroups at once), PC_EHIP.
+ */
+#define PC_LINKED_GROUPS 256
+#define PC_LINKED_STATUS_WORD 256
+
+/* Workspace bytes pc_twoshot_linked needs for (n, k); 0 if n or k would be
+ * rejected by it.  For k == 0 it is the fixed part of the workspace. */
+PC_API size_t pc_twoshot_linked_workspace_bytes(int n, size_t k);
+
+PC_API pc_status pc_twoshot_linked(const uint16_t* const* inputs, int n, uint16_t* const* outs,
+                                   size_t k, uint32_t* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * pc_allgather_copy -- gather N shards of sequence-stamped blocks.

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.pc_abi_version() == 4
+    assert B.pc_abi_version() == 5
     assert B.pc_strerror(B.PC_OK) == "success"
     for st in (B.PC_EINVAL, B.PC_EALIGN, B.PC_EUNSUPPORTED, B.PC_EHIP, 12345):
         assert isinstance(B.pc_strerror(st), str) and B.pc_strerror(st)
@@ -119,6 +119,51 @@ def test_consume_validation(args, want):
 def test_twoshot_validation(args, want):
     assert B.pc_twoshot(stream=0, check=False, **args) == want
     assert B.pc_twoshot_fused(stream=0, check=False, **args) == want
+    ws = A + 4096 * MB
+    assert B.pc_twoshot_linked(workspace=ws, workspace_bytes=64 * MB, stream=0, check=False,
+                               **args) == want
+
+
+WS = A + 4096 * MB
+
+
+def linked_need(n, k):
+    return B.pc_twoshot_linked_workspace_bytes(n, k)
+
+
+def test_linked_workspace_bytes():
+    fixed = 4 * (B.PC_LINKED_GROUPS + 64)
+    assert linked_need(8, 0) == fixed
+    # 1 MiB per rank, n = 8: slices of 8192 chunks, 512-chunk tiles -> 128 tiles.
+    assert linked_need(8, 8 * 65536) == fixed + 4 * 128
+    # 256 KiB per rank: 256-chunk tiles -> 8 slices of 8 tiles.
+    assert linked_need(8, 8 * 16384) == fixed + 4 * 64
+    # A ragged slice rounds its tile count up: 3 slices of 257 chunks -> 2 tiles each.
+    assert linked_need(3, 3 * 8 * 257) == fixed + 4 * 6
+    # From 4 MiB per rank the tiles hold 1024 chunks: 8 slices of 32768 chunks.
+    assert linked_need(8, 1 << 21) == fixed + 4 * 8 * 32
+    for bad in [(0, 64), (9, 72), (4, 8 * 4 + 8), (2, (1 << 34) + 16)]:
+        assert linked_need(*bad) == 0
+
+
+@pytest.mark.parametrize("ws,ws_bytes,want", [
+    (0, 64 * MB, B.PC_EINVAL),                 # no workspace
+    (WS + 4, 64 * MB, B.PC_EALIGN),            # misaligned
+    (WS, None, B.PC_EINVAL),                   # one word too small
+    (OUT + 16, 64 * MB, B.PC_EINVAL),          # overlaps outs[0]
+    (A + 64 * MB - 64, 64 * MB, B.PC_EINVAL),  # overlaps inputs[0]'s tail and inputs[1]
+])
+def test_twoshot_linked_workspace_validation(ws, ws_bytes, want):
+    n, k = 4, 4 * 8 * 300
+    if ws_bytes is None:
+        ws_bytes = linked_need(n, k) - 4
+    assert B.pc_twoshot_linked(ptrs(n), ptrs(n, base=OUT), k, ws, workspace_bytes=ws_bytes,
+                               stream=0, check=False) == want
+
+
+def test_twoshot_linked_binding_needs_size_for_raw_workspace():
+    with pytest.raises(ValueError):
+        B.pc_twoshot_linked(ptrs(2), ptrs(2, base=OUT), 16, WS, stream=0)
 
 
 @pytest.mark.parametrize("args,want", [

@@ -260,48 +260,109 @@ def test_consume_ll_wrong_seq_and_late_arrival(B, D, orc):
 
 # ---- twoshot -------------------------------------------------------------------
 
-def gpu_twoshot(B, D, xs, fused=False):
+TWOSHOT_MODES = ["two", "fused", "linked"]
+
+
+def linked_workspace(B, n, k):
+    """A zero-filled workspace for pc_twoshot_linked (int32 words)."""
+    nbytes = B.pc_twoshot_linked_workspace_bytes(n, k)
+    assert nbytes > 0
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device="cuda:0")
+
+
+def check_linked_workspace(B, D, ws, calls):
+    """After `calls` calls every workgroup's call counter reads `calls` and
+    no wait was abandoned."""
+    w = D.down(ws, np.uint32)
+    assert np.all(w[:B.PC_LINKED_GROUPS] == calls), np.unique(w[:B.PC_LINKED_GROUPS])
+    assert w[B.PC_LINKED_STATUS_WORD] == 0
+
+
+def run_twoshot(B, ins, outs, k, mode, ws=None):
+    if mode == "two":
+        B.pc_twoshot(ins, outs, k)
+    elif mode == "fused":
+        B.pc_twoshot_fused(ins, outs, k)
+    else:
+        B.pc_twoshot_linked(ins, outs, k, ws)
+
+
+def gpu_twoshot(B, D, xs, mode="two"):
     k = xs[0].size
     ins = [D.up(x) for x in xs]
     outs = [D.filled(k, 0xFFFF) for _ in xs]
-    (B.pc_twoshot_fused if fused else B.pc_twoshot)(ins, outs, k)
-    return [D.down(o, np.uint16) for o in outs]
+    ws = linked_workspace(B, len(xs), k) if mode == "linked" else None
+    run_twoshot(B, ins, outs, k, mode, ws)
+    got = [D.down(o, np.uint16) for o in outs]
+    if ws is not None:
+        check_linked_workspace(B, D, ws, 1)
+    return got
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_twoshot_1m(B, D, orc, fused):
+@pytest.mark.parametrize("mode", TWOSHOT_MODES)
+def test_twoshot_1m(B, D, orc, mode):
     case = synth.C3_TWOSHOT_1M
-    say(case.name, "fused" if fused else "two launches")
+    say(case.name, mode)
     xs = case.inputs()
     want = orc.twoshot(xs)
-    got = gpu_twoshot(B, D, xs, fused)
+    got = gpu_twoshot(B, D, xs, mode)
     oneshot = gpu_reduce(B, D, xs)
     for g, w in zip(got, want):
         assert np.array_equal(g, w)
         assert np.array_equal(g, oneshot)
 
 
-@pytest.mark.parametrize("fused", [False, True])
+# Slices of 1 chunk, ragged tiles, and for the linked form every tile size
+# (1, 2 and 4 chunks per lane) with more tiles than its grid has workgroups.
+@pytest.mark.parametrize("mode", TWOSHOT_MODES)
 @pytest.mark.parametrize("n,slice_chunks", [(2, 1), (3, 257), (5, 256 * 4 + 3), (8, 300000 + 5),
-                                            (1, 100), (6, 2 * 262144 + 9), (3, 100003)])
-def test_twoshot_shapes(B, D, orc, n, slice_chunks, fused):
+                                            (1, 100), (6, 2 * 262144 + 9), (3, 100003),
+                                            (8, 512 * 40 + 17), (7, 1024 * 70 + 1)])
+def test_twoshot_shapes(B, D, orc, n, slice_chunks, mode):
     k = 8 * n * slice_chunks
-    say("twoshot", n, k, "fused" if fused else "")
+    say("twoshot", n, k, mode)
     xs = [synth.normal_bf16(800 + n, 0, r, k) for r in range(n)]
     want = orc.reduce(xs, threads=THREADS)
-    for g in gpu_twoshot(B, D, xs, fused):
+    for g in gpu_twoshot(B, D, xs, mode):
         assert np.array_equal(g, want)
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_twoshot_in_place(B, D, orc, fused):
+@pytest.mark.parametrize("mode", TWOSHOT_MODES)
+def test_twoshot_in_place(B, D, orc, mode):
     n, k = 4, 8 * 4 * 999
     xs = [synth.normal_bf16(900, 0, r, k) for r in range(n)]
     ins = [D.up(x) for x in xs]
-    (B.pc_twoshot_fused if fused else B.pc_twoshot)(ins, ins, k)
+    ws = linked_workspace(B, n, k) if mode == "linked" else None
+    run_twoshot(B, ins, ins, k, mode, ws)
     want = orc.reduce(xs)
     for t in ins:
         assert np.array_equal(D.down(t, np.uint16), want)
+
+
+def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
+    """One workspace, many calls of different n and k (tile geometry changes
+    between calls): the flags of earlier calls are never taken as ready, and
+    every workgroup's counter advances once per call."""
+    shapes = [(8, 8 * 65536), (3, 3 * 8 * 5000), (8, 8 * 65536), (8, 8 * 8 * 1024 * 70),
+              (2, 16), (5, 5 * 8 * 256 * 3)]
+    nbytes = max(B.pc_twoshot_linked_workspace_bytes(n, k) for n, k in shapes)
+    ws = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    for i, (n, k) in enumerate(shapes):
+        say("linked reuse", i, n, k)
+        xs = [synth.uniform_bf16(1500 + i, 0, r, k) for r in range(n)]
+        ins = [D.up(x) for x in xs]
+        outs = [D.filled(k, 0xFFFF) for _ in range(n)]
+        B.pc_twoshot_linked(ins, outs, k, ws)
+        want = orc.reduce(xs, threads=THREADS)
+        for o in outs:
+            assert np.array_equal(D.down(o, np.uint16), want), (i, n, k)
+        check_linked_workspace(B, D, ws, i + 1)
+
+
+def test_twoshot_linked_empty_call_leaves_counters(B, D):
+    ws = linked_workspace(B, 4, 0)
+    B.pc_twoshot_linked([0] * 4, [0] * 4, 0, ws)
+    check_linked_workspace(B, D, ws, 0)
 
 
 # ---- all-gather copy -------------------------------------------------------------
@@ -499,6 +560,11 @@ def test_graph_replays_match_oracle(B, D, orc):
     lines = [torch.empty(lines_k // 2, dtype=torch.int64, device="cuda:0") for _ in range(n)]
     ll_out = torch.empty(lines_k, dtype=torch.int16, device="cuda:0")
     ll_bm = torch.empty(lines_k // 128, dtype=torch.int64, device="cuda:0")
+    louts = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
+    ws = linked_workspace(B, n, k)
+    for t in ins:
+        t.zero_()
+    B.pc_twoshot_linked(ins, louts, k, ws)       # one eager call before capture
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -509,6 +575,8 @@ def test_graph_replays_match_oracle(B, D, orc):
             for r in range(n):
                 B.pc_pack_ll(ins[r], lines[r], lines_k, 9)
             B.pc_consume_ll(lines, ll_out, lines_k, 9, ll_bm)
+            B.pc_twoshot_linked(ins, louts, k, ws)   # twice: the epoch advances
+            B.pc_twoshot_linked(ins, louts, k, ws)   # on the device, not the host
     torch.cuda.synchronize()
     for rep in range(4):
         xs = [synth.normal_bf16(1200 + rep, 0, r, k) for r in range(n)]
@@ -524,6 +592,11 @@ def test_graph_replays_match_oracle(B, D, orc):
         wo, wb = orc.consume_ll([orc.pack_ll(x[:lines_k], 9) for x in xs], lines_k, 9)
         assert np.array_equal(D.down(ll_out, np.uint16), wo), rep
         assert np.array_equal(D.down(ll_bm, np.uint64), wb), rep
+        for o in louts:
+            assert np.array_equal(D.down(o, np.uint16), want), rep
+        check_linked_workspace(B, D, ws, 1 + 2 * (rep + 1))
+        for o in louts:
+            o.fill_(-1)                           # the next replay must rewrite them
 
 
 def test_two_streams_disjoint_buffers(B, D, orc):
