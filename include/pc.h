@@ -4,9 +4,11 @@
  * The library implements one GPU's share of the all-reduce / all-gather
  * datapath: an N-way elementwise reduction of N rank-staged bf16 buffers in a
  * fixed rank order, sequence-number ("LL") line packing and consume-side
- * readiness validation, the twoshot split (slice reduce, then copy-out), and
- * an all-gather copy whose blocks carry sequence-number headers.  The N
- * peers' staged buffers are N distinct device regions.
+ * readiness validation, sentinel readiness, a speculative reduce validated by
+ * folded flags, the twoshot split (slice reduce, then copy-out; also in one
+ * launch, with or without flags between the phases), and an all-gather copy
+ * whose blocks carry sequence-number headers.  The N peers' staged buffers
+ * are N distinct device regions.
  *
  * Conventions shared by every call:
  *  - All functions are extern "C", return pc_status and never throw.
@@ -15,7 +17,8 @@
  *    arrays, read only during the call.  The pointers inside them and every
  *    other data pointer are DEVICE pointers on the current HIP device, each
  *    16-byte aligned.  The caller allocates and frees all memory; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing and keeps no state between calls (pc_twoshot_linked
+ *    keeps its call counters in a workspace the caller owns).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously; outputs are valid once the stream has
  *    reached the call.  No call synchronizes the device.
