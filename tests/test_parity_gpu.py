@@ -339,6 +339,25 @@ def test_twoshot_in_place(B, D, orc, mode):
         assert np.array_equal(D.down(t, np.uint16), want)
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_bandwidth_regime_every_n(B, D, orc, n):
+    """Every rank count in the persistent (bandwidth-regime) kernels: a
+    working set just past 64 MiB with ragged slices, for the reduce with a
+    permuted order and for all three twoshot forms."""
+    sc = -(-(4 << 20) // (n * (n + 1))) + 3          # chunks per slice
+    k = 8 * n * sc
+    say("bandwidth regime", n, k)
+    xs = [synth.normal_bf16(1600 + n, 0, r, k) for r in range(n)]
+    order = list(np.random.default_rng(40 + n).permutation(n))
+    assert np.array_equal(gpu_reduce(B, D, xs, order=order),
+                          orc.reduce(xs, order=order, threads=THREADS))
+    want = orc.reduce(xs, threads=THREADS)
+    for mode in TWOSHOT_MODES:
+        for g in gpu_twoshot(B, D, xs, mode):
+            assert np.array_equal(g, want), mode
+    torch.cuda.empty_cache()
+
+
 def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
     """One workspace, many calls of different n and k (tile geometry changes
     between calls): the flags of earlier calls are never taken as ready, and
