@@ -200,6 +200,9 @@ def test_pack_ll_bits(B, D, orc):
     x = synth.uniform_bf16(500, 0, 0, 8 * (512 * 3 + 7))
     assert np.array_equal(D.down(gpu_pack(B, D, x, 0xDEADBEEF), np.uint64),
                           orc.pack_ll(x, 0xDEADBEEF))
+    # Past 4 MiB per rank (two chunks per lane), with a ragged tail.
+    x = synth.uniform_bf16(501, 0, 0, 8 * ((1 << 18) + 7))
+    assert np.array_equal(D.down(gpu_pack(B, D, x, 3), np.uint64), orc.pack_ll(x, 3))
 
 
 def gpu_consume(B, D, lines_dev, k, seq, out_fill=0xFFFF):
@@ -224,7 +227,10 @@ def test_consume_ll_128k_stale(B, D, orc):
     assert 0.6 * case.lines < ready < 0.72 * case.lines
 
 
-@pytest.mark.parametrize("n,k", [(1, 128), (2, 128 * 3), (3, 128 * 37), (8, 128 * 1001), (5, 1 << 20)])
+# The last two shapes pass 4 MiB per rank (two 64-line groups per lane) and
+# end in a partial workgroup.
+@pytest.mark.parametrize("n,k", [(1, 128), (2, 128 * 3), (3, 128 * 37), (8, 128 * 1001), (5, 1 << 20),
+                                 (8, (1 << 21) + 128 * 5), (3, (1 << 22) + 128 * 3)])
 def test_consume_ll_shapes(B, D, orc, n, k):
     case = synth.LLCase("shape", 600 + n, n, k, stale_frac=0.03)
     staged = stage_oracle(orc, case)
@@ -452,6 +458,9 @@ def test_publish_sentinel_bits(B, D, orc):
     t = D.up(x)                                          # in place
     B.pc_publish_sentinel(t, t, x.size)
     assert np.array_equal(D.down(t, np.uint16), orc.publish_sentinel(x))
+    # Past 4 MiB per rank (two chunks per lane), with a ragged tail.
+    x = synth.SentinelCase("pub big", 74, 1, 8 * ((1 << 18) + 5)).payloads()[0]
+    assert np.array_equal(D.down(gpu_publish(B, D, x), np.uint16), orc.publish_sentinel(x))
 
 
 def test_consume_sentinel_128k_workload(B, D, orc):
@@ -474,7 +483,8 @@ def test_consume_sentinel_128k_workload(B, D, orc):
     assert 0.6 * case.packs < ready < 0.7 * case.packs
 
 
-@pytest.mark.parametrize("n,k", [(1, 512), (2, 512 * 3), (3, 512 * 37), (5, 512 * 129), (8, 1 << 20)])
+@pytest.mark.parametrize("n,k", [(1, 512), (2, 512 * 3), (3, 512 * 37), (5, 512 * 129), (8, 1 << 20),
+                                 (8, (1 << 21) + 512 * 3)])
 def test_consume_sentinel_shapes(B, D, orc, n, k):
     case = synth.SentinelCase("shape", 73 + n, n, k, 0.03, 0.01, 0.01)
     slots = [synth.unarrive(orc.publish_sentinel(x), m, t)
