@@ -64,14 +64,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, ui
                                              kRsrcWord3);
 }
 
+// 16-byte buffer load / store at `byte_off` with cache policy kPolicy (0 =
+// default).  A resource of zero bytes turns every store into a no-op, which
+// lets a loop over destinations skip one of them without a branch.
+template <int kPolicy>
+__device__ __forceinline__ u32x4 load16_rsrc(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kPolicy));
+}
+
+template <int kPolicy>
+__device__ __forceinline__ void store16_rsrc(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rs, byte_off, 0, kPolicy);
+}
+
 __device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
-    return __builtin_bit_cast(u32x4,
-                              __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kPolicyNonTemporal));
+    return load16_rsrc<kPolicyNonTemporal>(rs, byte_off);
 }
 
 __device__ __forceinline__ void store16_tile(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, u32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rs, byte_off, 0,
-                                           kPolicyDeviceScope);
+    store16_rsrc<kPolicyDeviceScope>(rs, byte_off, v);
 }
 
 // ---- bf16 <-> fp32 ----------------------------------------------------------

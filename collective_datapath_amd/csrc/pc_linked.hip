@@ -46,11 +46,6 @@ namespace pcdp {
 constexpr int kLinkBlock = 256;
 constexpr uint32_t kMaxPolls = 1u << 20;
 
-template <int kPolicy>
-__device__ __forceinline__ u32x4 load16_policy(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kPolicy));
-}
-
 // Chunks of tile j of a slice of `slice_chunks` chunks, as a byte count.
 template <uint32_t kTile>
 __device__ __forceinline__ uint32_t tile_bytes(size_t slice_chunks, size_t j) {
@@ -92,7 +87,7 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + c0, bytes);
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    v[u][r] = load16_policy<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
+                    v[u][r] = load16_rsrc<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
             }
             const __amdgpu_buffer_rsrc_t ro = tile_rsrc(outs.p[s] + c0, bytes);
 #pragma unroll
@@ -136,7 +131,7 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(outs.p[s] + c0, bytes);
                 u32x4 v[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = load16_policy<0>(rs, (u * kLinkBlock + tid) * 16u);
+                for (int u = 0; u < U; ++u) v[u] = load16_rsrc<0>(rs, (u * kLinkBlock + tid) * 16u);
                 // The owner's own range gets a zero-length resource, so its
                 // stores are dropped without a branch.
 #pragma unroll

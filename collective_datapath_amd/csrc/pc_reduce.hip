@@ -172,7 +172,10 @@ void k_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nsli
 
 // ---- twoshot copy-out: the owner's slice goes to every other rank's output ----
 // Grid: x = tile within a slice, y = slice s.  Reads outs[s] once per chunk
-// and writes it to the N-1 other outputs.
+// and writes it to the N-1 other outputs.  Tile-sized buffer resources clamp
+// the ragged last tile, and the owner's own range gets a zero-length
+// resource, so a lane's N-1 stores issue back to back with no branch (a
+// branch per destination made each store wait for the one before it).
 template <int N, int U>
 __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t nslice) {
     constexpr uint32_t kTile = kBlock * U;
@@ -180,23 +183,17 @@ __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t 
     const uint32_t tile0 = blockIdx.x * kTile;
     const size_t first = (size_t)s * nslice + tile0;
     const uint32_t left = nslice - tile0;
+    const uint32_t bytes = (left < kTile ? left : kTile) * 16u;
     const uint32_t t = threadIdx.x;
-    const u32x4* from = outs.p[s] + first;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(outs.p[s] + first, bytes);
     u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t c = u * kBlock + t;
-        if (left >= kTile || c < left) v[u] = from[c];
-    }
+    for (int u = 0; u < U; ++u) v[u] = load16_rsrc<0>(rs, (u * kBlock + t) * 16u);
 #pragma unroll
     for (int r = 0; r < N; ++r) {
-        if ((uint32_t)r == s) continue;
-        u32x4* to = outs.p[r] + first;
+        const __amdgpu_buffer_rsrc_t rd = tile_rsrc(outs.p[r] + first, (uint32_t)r == s ? 0u : bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t c = u * kBlock + t;
-            if (left >= kTile || c < left) to[c] = v[u];
-        }
+        for (int u = 0; u < U; ++u) store16_rsrc<0>(rd, (u * kBlock + t) * 16u, v[u]);
     }
 }
 
