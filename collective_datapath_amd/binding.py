@@ -28,6 +28,7 @@ PC_BLOCK_RECORD_BYTES = 136
 EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
            "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated", "pc_strerror", "pc_abi_version")
+PC_ABI_VERSION = 5          # the include/pc.h this binding is written against
 PC_MAX_ATTEMPTS = 65536
 PC_LINKED_GROUPS = 256
 PC_LINKED_STATUS_WORD = 256
