@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604518152,
+TRAFFIC = {"bytes": 604518132,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "d5fafd616fcbada31a1f03f08e86e1e94c59d1f37a6b1abf1bde28647ab0b7cf"}
+           "sha256": "9139d9dfcc413259f4bff60b6fdd5b647aba32ad3153cfa0700f8004856d23a3"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="timed calls of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
-                    choices=["all", "headline", "c1", "c1v", "c2", "c2s", "c3", "c5", "sweep",
+                    choices=["all", "headline", "c1", "c1v", "c2", "c2s", "c3", "c5", "atom_copy", "sweep",
                              "sweep_cold", "copy"],
                     help="run one part only (profiling); 'copy' times a plain device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -395,6 +395,31 @@ def run_c3(d, B, synth, oracle, args, out):
     out["configs"]["twoshot_linked_1m"]["waits_abandoned"] = int(ws[B.PC_LINKED_STATUS_WORD])
 
 
+def run_copy_atom(d, B, synth, oracle, args, out):
+    """The Atom copy: 256 MiB (HBM-bound, event-timed) and 1 MiB (per call
+    in a graph, cache-resident).  Parity: the destination equals the source."""
+    torch = d.torch
+    for name, nbytes in (("atom_copy_256m", 256 << 20), ("atom_copy_1m", 1 << 20)):
+        g = torch.Generator(device=d.dev)
+        g.manual_seed(nbytes % 1000003)
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=d.dev, generator=g)
+        dst = torch.zeros_like(src)
+        fn = lambda: B.pc_copy(dst, src, nbytes)  # noqa: E731
+        if nbytes >= (64 << 20):
+            ms = d.events_ms(fn, 50, 5)
+            t = {"event_us_per_launch": round(ms * 1e3, 3), "bytes_per_call": 2 * nbytes,
+                 "gbs": round(gbs(2 * nbytes, ms * 1e3), 1)}
+        else:
+            t = timing(d, fn, 1000, 50)
+            t.update(bytes_per_call=2 * nbytes,
+                     gbs_cache_resident=round(gbs(2 * nbytes, t["graph_us"]), 1))
+        out["configs"][name] = t
+        if oracle is not None:
+            torch.cuda.synchronize()
+            out["parity"][name] = bool(torch.equal(dst, src))
+        del src, dst
+
+
 def run_c5(d, B, synth, oracle, args, out):
     case = synth.C5_ALLGATHER_2M
     recs, masks = case.records()
@@ -537,7 +562,8 @@ def main():
     if args.only == "copy":
         run_copy(d, out, args.steps)
     for name, fn in (("c1", run_c1), ("c1v", run_c1v), ("c2", run_c2), ("c2s", run_c2s), ("c3", run_c3),
-                     ("c5", run_c5), ("sweep", run_sweep), ("sweep_cold", run_sweep_cold)):
+                     ("c5", run_c5), ("atom_copy", run_copy_atom), ("sweep", run_sweep),
+                     ("sweep_cold", run_sweep_cold)):
         if args.only in ("all", name):
             log("running", name)
             fn(d, B, synth, oracle, args, out)

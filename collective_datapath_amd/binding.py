@@ -25,10 +25,10 @@ PC_BLOCK_PAYLOAD_BYTES = 128
 PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
-EXPORTS = ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
+EXPORTS = ("pc_copy", "pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
            "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated", "pc_strerror", "pc_abi_version")
-PC_ABI_VERSION = 5          # the include/pc.h this binding is written against
+PC_ABI_VERSION = 6          # the include/pc.h this binding is written against
 PC_MAX_ATTEMPTS = 65536
 PC_LINKED_GROUPS = 256
 PC_LINKED_STATUS_WORD = 256
@@ -64,6 +64,7 @@ if len(_hip_runtimes()) > 1:
     raise ImportError("two HIP runtimes are mapped in this process "
                       f"({sorted(_hip_runtimes())}); import torch before loading libpcdp.so")
 _P, _S, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_lib.pc_copy.argtypes = [_P, _P, _S, _P]
 _lib.pc_reduce.argtypes = [_P, _I, _P, _S, _P, _P]
 _lib.pc_pack_ll.argtypes = [_P, _P, _S, ctypes.c_uint32, _P]
 _lib.pc_consume_ll.argtypes = [_P, _I, _P, _S, ctypes.c_uint32, _P, _P]
@@ -76,7 +77,7 @@ _lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
 _lib.pc_publish_sentinel.argtypes = [_P, _P, _S, _P]
 _lib.pc_reduce_validated.argtypes = [_P, _P, _I, _P, _S, _S, ctypes.c_uint32, ctypes.c_uint32, _P, _P]
 _lib.pc_consume_sentinel.argtypes = [_P, _I, _P, _S, _P, _P]
-for _f in ("pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
+for _f in ("pc_copy", "pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
            "pc_twoshot_linked", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated"):
     getattr(_lib, _f).restype = _I
@@ -143,6 +144,11 @@ def pc_strerror(status: int) -> str:
 
 def pc_abi_version() -> int:
     return _lib.pc_abi_version()
+
+
+def pc_copy(dst: Buffer, src: Buffer, nbytes: int, stream=None, check: bool = True) -> int:
+    st = _lib.pc_copy(_addr(dst, nbytes, "dst"), _addr(src, nbytes, "src"), nbytes, _stream(stream))
+    return _call("pc_copy", st, check)
 
 
 def pc_reduce(inputs: Sequence[Buffer], out: Buffer, k: int, order: Optional[Sequence[int]] = None,

@@ -70,6 +70,17 @@ pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t 
     return from_hip(pcdp::launch_reduce(src, n, out, k / 8, static_cast<hipStream_t>(stream)));
 }
 
+pc_status pc_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (bytes > 2 * PC_MAX_ELEMS) return PC_EINVAL;
+    if (bytes % 16) return PC_EALIGN;
+    if (bytes == 0) return PC_OK;
+    if (!dst || !src) return PC_EINVAL;
+    if (!aligned16(dst) || !aligned16(src)) return PC_EALIGN;
+    if (dst == src) return PC_OK;  // copying a range onto itself changes nothing
+    if (overlaps(dst, bytes, src, bytes)) return PC_EINVAL;
+    return from_hip(pcdp::launch_copy(src, dst, bytes / 16, static_cast<hipStream_t>(stream)));
+}
+
 pc_status pc_pack_ll(const uint16_t* src, uint64_t* dst, size_t k, uint32_t seq, void* stream) {
     if (seq == 0 || k > PC_MAX_ELEMS) return PC_EINVAL;
     if (k % 8) return PC_EALIGN;

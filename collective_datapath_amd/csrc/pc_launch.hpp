@@ -12,6 +12,12 @@
 
 namespace pcdp {
 
+// Compute units of the current device, cached per device.
+uint32_t device_cus();
+
+// Atom copy of nchunks 16-byte chunks, bytes unchanged.
+hipError_t launch_copy(const void* src, void* dst, size_t nchunks, hipStream_t stream);
+
 // out[c] = fold over ranks of src[r][c], for 16-byte chunks c < nchunks.
 // src has n pointers already permuted into fold order.
 hipError_t launch_reduce(const void* const* src, int n, void* out, size_t nchunks,

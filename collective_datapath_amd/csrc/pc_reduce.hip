@@ -203,8 +203,9 @@ __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t 
 // a working set of 64 MiB or more use the persistent kernel above.
 enum class Regime { kSmall, kMid, kStream };
 
-// Compute units of the current device, looked up once per device.
-static uint32_t device_cus() {
+// Compute units of the current device, looked up once per device (256 if
+// the query fails).
+uint32_t device_cus() {
     static int cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

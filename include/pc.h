@@ -2,7 +2,7 @@
  * pc.h -- C ABI of the MI355X collective datapath library (libpcdp.so).
  *
  * The library implements one GPU's share of the all-reduce / all-gather
- * datapath: an N-way elementwise reduction of N rank-staged bf16 buffers in a
+ * datapath: the Atom's byte-range copy, an N-way elementwise reduction of N rank-staged bf16 buffers in a
  * fixed rank order, sequence-number ("LL") line packing and consume-side
  * readiness validation, sentinel readiness, a speculative reduce validated by
  * folded flags, the twoshot split (slice reduce, then copy-out; also in one
@@ -69,7 +69,7 @@ enum {
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 5
+#define PC_ABI_VERSION 6
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -95,6 +95,21 @@ enum {
  */
 PC_API pc_status pc_reduce(const uint16_t* const* inputs, int n, uint16_t* out, size_t k,
                     const int32_t* order, void* stream);
+
+/*
+ * pc_copy -- the Atom's copy: `bytes` bytes from src to dst, unchanged.
+ * Source: Purlin, Section 3.3 (the Atom's two primitives are a copy of one
+ * contiguous range and a typed reduce; the copy's per-element step is a
+ * store).  The copy-outs of pc_twoshot and pc_allgather_copy are this
+ * primitive with a fan-out or a readiness test added.
+ *   dst, src : device, 16-byte aligned; disjoint, or exactly equal (then
+ *              nothing is launched).
+ *   bytes    : multiple of 16, at most 2*PC_MAX_ELEMS.
+ * Every bit pattern is copied as is (NaN payloads included).
+ * Errors: PC_EINVAL (NULL pointer, partial overlap, bytes above the maximum),
+ * PC_EALIGN, PC_EHIP.
+ */
+PC_API pc_status pc_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 /*
  * pc_pack_ll -- stage k bf16 values as k/2 sequence-stamped 8-byte lines.

@@ -4,6 +4,7 @@
  * runtime API, streams are the null stream.
  *
  * Expected values are closed forms, not outputs of the library:
+ *  - a copy returns its source bytes (Purlin, Section 3.3);
  *  - a fold of exactly representable values (rank r holds (r+1)/8) has an
  *    exact sum (Purlin, Section 3.3, Equation (2));
  *  - the cancellation triple (2^25, 1, -2^25) gives +0 in order (0,1,2) and
@@ -237,6 +238,27 @@ static void check_allgather_concat(void) {
     free(got);
 }
 
+/* The Atom copy moves every byte pattern unchanged (NaN payloads too). */
+static void check_copy(void) {
+    const size_t bytes = 16 * (256 * 4 + 9);
+    uint8_t* h = host_alloc(bytes);
+    uint8_t* back = host_alloc(bytes);
+    for (size_t i = 0; i < bytes; ++i) h[i] = (uint8_t)(i * 37 + (i >> 8));
+    uint8_t* src = dev_alloc(bytes);
+    uint8_t* dst = dev_alloc(bytes);
+    HIP_OK(hipMemcpy(src, h, bytes, hipMemcpyHostToDevice));
+    HIP_OK(hipMemset(dst, 0, bytes));
+    EXPECT(pc_copy(dst, src, bytes, NULL) == PC_OK, "pc_copy status");
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(back, dst, bytes, hipMemcpyDeviceToHost));
+    EXPECT(memcmp(back, h, bytes) == 0, "pc_copy bytes unchanged");
+    EXPECT(pc_copy(dst, dst + 16, 64, NULL) == PC_EINVAL, "pc_copy partial overlap");
+    HIP_OK(hipFree(src));
+    HIP_OK(hipFree(dst));
+    free(h);
+    free(back);
+}
+
 /* Rejected calls return their status codes; empty calls are no-ops. */
 static void check_statuses(void) {
     uint16_t* a = dev_alloc(4096);
@@ -262,6 +284,7 @@ int main(void) {
     }
     EXPECT(pc_abi_version() == PC_ABI_VERSION, "ABI version");
     check_statuses();
+    check_copy();
     check_reduce_exact_sums();
     check_cancellation();
     check_ll_identity();

@@ -246,3 +246,19 @@ def test_binding_rejects_host_and_short_tensors():
         B.pc_reduce([cpu, cpu], cpu, 64, stream=0)
     with pytest.raises(ValueError):
         B.pc_publish_sentinel(cpu, cpu, 64, stream=0)
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(dst=0, src=A, nbytes=16), B.PC_EINVAL),
+    (dict(dst=OUT, src=0, nbytes=16), B.PC_EINVAL),
+    (dict(dst=OUT + 8, src=A, nbytes=16), B.PC_EALIGN),
+    (dict(dst=OUT, src=A + 4, nbytes=16), B.PC_EALIGN),
+    (dict(dst=OUT, src=A, nbytes=24), B.PC_EALIGN),
+    (dict(dst=A + 16, src=A, nbytes=64), B.PC_EINVAL),            # partial overlap
+    (dict(dst=A, src=A + 48, nbytes=64), B.PC_EINVAL),
+    (dict(dst=OUT, src=A, nbytes=(1 << 35) + 16), B.PC_EINVAL),   # above the maximum
+    (dict(dst=A, src=A, nbytes=4096), B.PC_OK),                    # onto itself: no-op
+    (dict(dst=0, src=0, nbytes=0), B.PC_OK),                       # empty
+])
+def test_copy_validation(args, want):
+    assert B.pc_copy(stream=0, check=False, **args) == want

@@ -169,6 +169,32 @@ def test_reduce_large_offsets_sampled(B, D, orc):
     torch.cuda.empty_cache()
 
 
+# ---- Atom copy -------------------------------------------------------------------
+
+# One chunk; whole tiles plus a ragged tail (small and mid shapes); the
+# bandwidth regime from a 64 MiB working set, with a ragged last batch.
+@pytest.mark.parametrize("nbytes", [16, 16 * (256 * 3 + 5), (4 << 20) + 16 * 3, (32 << 20) + 16 * 1029,
+                                    (96 << 20) + 16 * 77])
+def test_copy_bytes_unchanged(B, D, nbytes):
+    """Every byte arrives unchanged: the expected value is the source itself
+    (NaN payloads, subnormals and all other patterns included)."""
+    say("copy", nbytes)
+    src = np.random.default_rng(nbytes % 1000003).integers(0, 256, nbytes, dtype=np.uint8)
+    s = D.up(src)
+    d = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    B.pc_copy(d, s, nbytes)
+    assert np.array_equal(D.down(d, np.uint8), src)
+
+
+def test_copy_into_a_window_leaves_the_rest(B, D):
+    src = np.random.default_rng(5).integers(0, 256, 4096, dtype=np.uint8)
+    d = torch.full((8192,), 0x3C, dtype=torch.uint8, device="cuda:0")
+    B.pc_copy(d[1024:], D.up(src), 4096)
+    got = D.down(d, np.uint8)
+    assert np.array_equal(got[1024:5120], src)
+    assert np.all(got[:1024] == 0x3C) and np.all(got[5120:] == 0x3C)
+
+
 # ---- LL pack / consume ---------------------------------------------------------
 
 def gpu_pack(B, D, x, seq):
