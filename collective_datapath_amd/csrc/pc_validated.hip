@@ -21,13 +21,31 @@ namespace pcdp {
 
 constexpr int kVBlock = 256;
 
-// The first attempt reads with the default policy; a retry must not be
-// served stale data from this CU's cache, so it reads device-coherently.
-__device__ __forceinline__ u32x4 load16_attempt(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off,
-                                                bool retry) {
-    return __builtin_bit_cast(
-        u32x4, retry ? __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kPolicyDeviceScope)
-                     : __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+// One attempt's reads.  The first attempt reads payload and flags the
+// default way, so they may come from the caches; a stale cached flag holds
+// an earlier call's value, which only makes the check fail.  A retry must
+// not be served stale data, so it reads both device-coherently.  Policy and
+// scope are template parameters, so each attempt is one straight block of
+// loads.
+template <int N, int U, int kPolicy>
+__device__ __forceinline__ void load_payload(u32x4 (&v)[U][N], const Ptrs<const u32x4*>& src,
+                                             size_t first, uint32_t t) {
+    constexpr uint32_t kTile = kVBlock * U;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, kTile * 16u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u][r] = load16_rsrc<kPolicy>(rs, (u * kVBlock + t) * 16u);
+    }
+}
+
+// The validation fold: the uint32 sum (mod 2^32) of every rank's flag b.
+template <int N, int kScope>
+__device__ __forceinline__ uint32_t fold_flags(const Ptrs<const uint32_t*>& flags, uint32_t b) {
+    uint32_t folded = 0;
+#pragma unroll
+    for (int r = 0; r < N; ++r) folded += __hip_atomic_load(flags.p[r] + b, __ATOMIC_RELAXED, kScope);
+    return folded;
 }
 
 // U = elems_per_flag / 2048: each lane folds U chunks of the tile.
@@ -37,25 +55,18 @@ __global__ __launch_bounds__(kVBlock) void k_reduce_validated(Ptrs<const u32x4*>
                                                                u32x4* out, uint32_t flag,
                                                                uint32_t max_attempts,
                                                                uint32_t* attempts) {
-    constexpr uint32_t kTile = kVBlock * U;  // chunks per tile
     __shared__ uint32_t verdict;
     const uint32_t b = blockIdx.x, t = threadIdx.x;
-    const size_t first = (size_t)b * kTile;
+    const size_t first = (size_t)b * (kVBlock * U);
     const uint32_t expect = (uint32_t)N * flag;
     uint32_t accepted = 0;
     for (uint32_t a = 1; a <= max_attempts; ++a) {
         u32x4 v[U][N];
-#pragma unroll
-        for (int r = 0; r < N; ++r) {
-            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, kTile * 16u);
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u][r] = load16_attempt(rs, (u * kVBlock + t) * 16u, a > 1);
-        }
+        if (a == 1) load_payload<N, U, 0>(v, src, first, t);
+        else load_payload<N, U, kPolicyDeviceScope>(v, src, first, t);
         if (t == 0) {
-            uint32_t folded = 0;
-#pragma unroll
-            for (int r = 0; r < N; ++r)
-                folded += __hip_atomic_load(flags.p[r] + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t folded = a == 1 ? fold_flags<N, __HIP_MEMORY_SCOPE_WORKGROUP>(flags, b)
+                                           : fold_flags<N, __HIP_MEMORY_SCOPE_AGENT>(flags, b);
             verdict = folded == expect;
         }
         __syncthreads();
