@@ -124,6 +124,22 @@ def test_reduce_specials_three_ranks(B, D, orc):
         assert np.array_equal(gpu_reduce(B, D, xs, order=order), orc.reduce(xs, order=order))
 
 
+def test_reduce_three_ranks_random_patterns(B, D, orc):
+    """2^26 triples of uniformly random bf16 bit patterns (every sign,
+    exponent and payload, NaNs and infinities included), in two orders."""
+    k = 1 << 26
+    say("random triples", k)
+    rng = np.random.default_rng(26)
+    xs = [rng.integers(0, 1 << 16, k, dtype=np.uint32).astype(np.uint16) for _ in range(3)]
+    for order in ([0, 1, 2], [1, 2, 0]):
+        want = orc.reduce(xs, order=order, threads=THREADS)
+        got = gpu_reduce(B, D, xs, order=order)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, [(hex(xs[0][i]), hex(xs[1][i]), hex(xs[2][i]), hex(got[i]), hex(want[i]))
+                               for i in bad[:8]]
+    torch.cuda.empty_cache()
+
+
 def test_reduce_in_place(B, D, orc):
     n, k = 4, 8 * 5000
     xs = [synth.uniform_bf16(400, 0, r, k) for r in range(n)]
