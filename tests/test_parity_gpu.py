@@ -211,6 +211,36 @@ def test_copy_into_a_window_leaves_the_rest(B, D):
     assert np.all(got[:1024] == 0x3C) and np.all(got[5120:] == 0x3C)
 
 
+def test_maximum_size_reduce_and_copy(B, D, orc):
+    """k = PC_MAX_ELEMS (32 GiB per rank) at N = 2, then a copy of the
+    largest size pc_copy accepts (2 * PC_MAX_ELEMS bytes): outputs sampled at
+    both ends, around every power-of-two byte offset from 4 GiB and at random
+    points, against the oracle on the sampled inputs (copy: the source)."""
+    k = 1 << 34
+    need = 3 * 2 * k + (2 << 30)
+    free, _ = torch.cuda.mem_get_info()
+    if free < need:
+        pytest.skip(f"needs {need >> 30} GiB of free device memory, {free >> 30} GiB free")
+    say("maximum size", 2, k)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(34)
+    ins = [torch.empty(k, dtype=torch.int16, device="cuda:0").random_(-32768, 32767, generator=g)
+           for _ in range(2)]
+    out = torch.empty(k, dtype=torch.int16, device="cuda:0")
+    B.pc_reduce(ins, out, k)
+    edges = [(1 << b) // 2 for b in range(32, 36)]  # element index at byte offsets 4, 8, 16, 32 GiB
+    idx = np.concatenate([np.arange(0, 8192), np.arange(k - 8192, k)] +
+                         [np.arange(max(e - 512, 0), min(e + 512, k)) for e in edges] +
+                         [np.random.default_rng(34).integers(0, k, 1 << 16)])
+    it = torch.from_numpy(idx).to("cuda:0")
+    xs = [D.down(t[it], np.uint16) for t in ins]
+    assert np.array_equal(D.down(out[it], np.uint16), orc.reduce(xs))
+    B.pc_copy(out, ins[1], 2 * k)
+    assert np.array_equal(D.down(out[it], np.uint16), xs[1])
+    del ins, out, it
+    torch.cuda.empty_cache()
+
+
 # ---- LL pack / consume ---------------------------------------------------------
 
 def gpu_pack(B, D, x, seq):
