@@ -98,34 +98,60 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-def _addr(b: Optional[Buffer], nbytes: int = 0, what: str = "buffer") -> int:
-    """Device address of `b`.  A tensor must live on the current GPU, be
+def _check_tensor(b, nbytes: int, what: str, dev: Optional[int] = None) -> None:
+    """A tensor handed to the library must live on the current GPU, be
     contiguous and hold at least `nbytes` bytes (what the call will touch);
-    anything else raises here instead of faulting on the device.  Raw int
+    anything else raises here instead of faulting on the device."""
+    where = b.get_device()  # -1 for host memory
+    if where < 0 or where != (torch.cuda.current_device() if dev is None else dev):
+        raise ValueError(f"{what} must be a tensor on the current GPU (got {b.device})")
+    if not b.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if b.nbytes < nbytes:
+        raise ValueError(f"{what} holds {b.nbytes} bytes; the call needs {nbytes}")
+
+
+def _addr(b: Optional[Buffer], nbytes: int = 0, what: str = "buffer") -> int:
+    """Device address of `b` (checked as above when nbytes > 0).  Raw int
     addresses are passed through unchecked."""
     if b is None:
         return 0
     if isinstance(b, int):
         return b
     if nbytes:
-        if not b.is_cuda or b.device.index != torch.cuda.current_device():
-            raise ValueError(f"{what} must be a tensor on the current GPU (got {b.device})")
-        if not b.is_contiguous():
-            raise ValueError(f"{what} must be contiguous")
-        have = b.numel() * b.element_size()
-        if have < nbytes:
-            raise ValueError(f"{what} holds {have} bytes; the call needs {nbytes}")
+        _check_tensor(b, nbytes, what)
     return b.data_ptr()
 
 
 def _addrs(bs: Sequence[Buffer], nbytes: int = 0, what: str = "buffer"):
-    return (ctypes.c_void_p * max(len(bs), 1))(
-        *[_addr(b, nbytes, f"{what}[{i}]") for i, b in enumerate(bs)])
+    """Host array of device addresses (each tensor checked as in _addr)."""
+    ptrs = []
+    dev = None
+    for i, b in enumerate(bs):
+        if b is None:
+            ptrs.append(0)
+        elif isinstance(b, int):
+            ptrs.append(b)
+        else:
+            if nbytes:
+                where = b.get_device()
+                if where >= 0 and dev is None:
+                    dev = torch.cuda.current_device()
+                if where < 0 or where != dev or not b.is_contiguous() or b.nbytes < nbytes:
+                    _check_tensor(b, nbytes, f"{what}[{i}]", dev)
+            ptrs.append(b.data_ptr())
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+
+
+# torch's current stream as a raw handle, without building a Stream object
+# (the public route costs a few microseconds per call).
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream) -> int:
     if stream is None:
-        import torch
+        if _current_raw_stream is not None:
+            return _current_raw_stream(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
