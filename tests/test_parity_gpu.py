@@ -718,6 +718,36 @@ def test_two_streams_disjoint_buffers(B, D, orc):
     assert all(np.array_equal(D.down(o, np.uint16), want) for o in ob)
 
 
+def test_twoshot_linked_next_to_a_persistent_kernel(B, D, orc):
+    """The linked twoshot launched while a bandwidth-regime reduce on another
+    stream holds the CUs: some of its workgroups start late, others wait on
+    flags meanwhile (bounded).  Results stay exact and no wait is abandoned."""
+    n, k = 8, 8 * 65536
+    big_k = 8 << 20                                   # 16 MiB per rank: persistent regime
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(77)
+    big = [torch.randint(-30000, 30000, (big_k,), dtype=torch.int16, device="cuda:0", generator=g)
+           for _ in range(n)]
+    big_out = torch.empty(big_k, dtype=torch.int16, device="cuda:0")
+    xs = [synth.normal_bf16(1700, 0, r, k) for r in range(n)]
+    ins = [D.up(x) for x in xs]
+    outs = [D.filled(k, 0xFFFF) for _ in range(n)]
+    ws = linked_workspace(B, n, k)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        B.pc_reduce(big, big_out, big_k, stream=sa)
+        B.pc_twoshot_linked(ins, outs, k, ws, stream=sb)
+    torch.cuda.synchronize()
+    want = orc.reduce(xs)
+    for o in outs:
+        assert np.array_equal(D.down(o, np.uint16), want)
+    check_linked_workspace(B, D, ws, 5)
+    idx = torch.arange(0, big_k, 4099, device="cuda:0")
+    assert np.array_equal(D.down(big_out[idx], np.uint16),
+                          orc.reduce([D.down(t[idx], np.uint16) for t in big]))
+
+
 def test_binding_rejects_bad_tensors_before_launch(B, D):
     k = 4096
     x = D.up(synth.uniform_bf16(1310, 0, 0, k))
