@@ -165,20 +165,24 @@ def _call(fn: str, status: int, check: bool) -> int:
 
 
 def pc_strerror(status: int) -> str:
+    """Text of a pc_status code."""
     return _lib.pc_strerror(status).decode()
 
 
 def pc_abi_version() -> int:
+    """PC_ABI_VERSION of the loaded library."""
     return _lib.pc_abi_version()
 
 
 def pc_copy(dst: Buffer, src: Buffer, nbytes: int, stream=None, check: bool = True) -> int:
+    """Atom copy: nbytes from src to dst, unchanged (include/pc.h, pc_copy)."""
     st = _lib.pc_copy(_addr(dst, nbytes, "dst"), _addr(src, nbytes, "src"), nbytes, _stream(stream))
     return _call("pc_copy", st, check)
 
 
 def pc_reduce(inputs: Sequence[Buffer], out: Buffer, k: int, order: Optional[Sequence[int]] = None,
               stream=None, check: bool = True) -> int:
+    """out = rank-ordered fold of the n inputs, k bf16 each; `order` permutes the fold order (include/pc.h, pc_reduce)."""
     if order is not None and len(order) != len(inputs):
         raise ValueError("order must list every rank exactly once")
     ordp = (ctypes.c_int32 * len(order))(*order) if order is not None else None
@@ -189,12 +193,14 @@ def pc_reduce(inputs: Sequence[Buffer], out: Buffer, k: int, order: Optional[Seq
 
 
 def pc_pack_ll(src: Buffer, dst: Buffer, k: int, seq: int, stream=None, check: bool = True) -> int:
+    """Pack k bf16 of src into k/2 LL lines stamped with seq (include/pc.h, pc_pack_ll)."""
     st = _lib.pc_pack_ll(_addr(src, 2 * k, "src"), _addr(dst, 4 * k, "dst"), k, seq, _stream(stream))
     return _call("pc_pack_ll", st, check)
 
 
 def pc_consume_ll(lines: Sequence[Buffer], out: Buffer, k: int, seq: int, ready_bitmap: Buffer,
                   stream=None, check: bool = True) -> int:
+    """Fold the lines every rank stamped with seq into out; one ready bit per line (include/pc.h, pc_consume_ll)."""
     st = _lib.pc_consume_ll(_addrs(lines, 4 * k, "lines"), len(lines), _addr(out, 2 * k, "out"), k,
                             seq, _addr(ready_bitmap, k // 128 * 8, "ready_bitmap"), _stream(stream))
     return _call("pc_consume_ll", st, check)
@@ -202,6 +208,7 @@ def pc_consume_ll(lines: Sequence[Buffer], out: Buffer, k: int, seq: int, ready_
 
 def pc_twoshot(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=None,
                check: bool = True) -> int:
+    """Twoshot in two launches: slice s folded into outs[s], then copied to every outs[r] (include/pc.h, pc_twoshot)."""
     if len(outs) != len(inputs):
         raise ValueError("pc_twoshot needs one output per input")
     st = _lib.pc_twoshot(_addrs(inputs, 2 * k, "inputs"), len(inputs), _addrs(outs, 2 * k, "outs"),
@@ -211,6 +218,7 @@ def pc_twoshot(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=
 
 def pc_twoshot_fused(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, stream=None,
                      check: bool = True) -> int:
+    """Twoshot in one launch: the folding workgroup writes every output (include/pc.h, pc_twoshot_fused)."""
     if len(outs) != len(inputs):
         raise ValueError("pc_twoshot_fused needs one output per input")
     st = _lib.pc_twoshot_fused(_addrs(inputs, 2 * k, "inputs"), len(inputs),
@@ -219,12 +227,15 @@ def pc_twoshot_fused(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, s
 
 
 def pc_twoshot_linked_workspace_bytes(n: int, k: int) -> int:
+    """Workspace bytes pc_twoshot_linked needs for (n, k); 0 if n or k is invalid."""
     return _lib.pc_twoshot_linked_workspace_bytes(n, k)
 
 
 def pc_twoshot_linked(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, workspace: Buffer,
                       workspace_bytes: Optional[int] = None, stream=None, check: bool = True) -> int:
-    """`workspace`: zero-filled before its first use, then reused unchanged
+    """Twoshot in one launch, phases linked per tile by epoch flags kept in
+    `workspace` (include/pc.h, pc_twoshot_linked).
+    `workspace`: zero-filled before its first use, then reused unchanged
     across calls.  `workspace_bytes` defaults to the size of a workspace
     tensor and must be given for a raw address."""
     if len(outs) != len(inputs):
@@ -243,6 +254,7 @@ def pc_twoshot_linked(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, 
 
 def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, seq: int,
                       ready_bitmap: Buffer, stream=None, check: bool = True) -> int:
+    """Copy the payload of every record whose header equals seq; one ready bit per block (include/pc.h, pc_allgather_copy)."""
     blocks = shard_bytes // PC_BLOCK_PAYLOAD_BYTES
     st = _lib.pc_allgather_copy(_addrs(shards, blocks * PC_BLOCK_RECORD_BYTES, "shards"), len(shards),
                                 _addr(out, len(shards) * shard_bytes, "out"), shard_bytes, seq,
@@ -252,6 +264,7 @@ def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, s
 
 
 def pc_publish_sentinel(src: Buffer, slot: Buffer, k: int, stream=None, check: bool = True) -> int:
+    """Publish k bf16 into sentinel-armed storage, sentinel values made canonical NaN (include/pc.h, pc_publish_sentinel)."""
     st = _lib.pc_publish_sentinel(_addr(src, 2 * k, "src"), _addr(slot, 2 * k, "slot"), k,
                                   _stream(stream))
     return _call("pc_publish_sentinel", st, check)
@@ -259,6 +272,7 @@ def pc_publish_sentinel(src: Buffer, slot: Buffer, k: int, stream=None, check: b
 
 def pc_consume_sentinel(slots: Sequence[Buffer], out: Buffer, k: int, ready_bitmap: Buffer,
                         stream=None, check: bool = True) -> int:
+    """Fold the packs no rank still holds the sentinel in, then re-arm them (include/pc.h, pc_consume_sentinel)."""
     st = _lib.pc_consume_sentinel(_addrs(slots, 2 * k, "slots"), len(slots), _addr(out, 2 * k, "out"),
                                   k, _addr(ready_bitmap, k // 512 * 8, "ready_bitmap"), _stream(stream))
     return _call("pc_consume_sentinel", st, check)
@@ -267,6 +281,7 @@ def pc_consume_sentinel(slots: Sequence[Buffer], out: Buffer, k: int, ready_bitm
 def pc_reduce_validated(inputs: Sequence[Buffer], flags: Sequence[Buffer], out: Buffer, k: int,
                         elems_per_flag: int, flag: int, max_attempts: int, attempts: Buffer,
                         stream=None, check: bool = True) -> int:
+    """Speculative reduce accepted per tile when the folded flags equal n * flag (include/pc.h, pc_reduce_validated)."""
     if len(flags) != len(inputs):
         raise ValueError("pc_reduce_validated needs one flag buffer per input")
     tiles = k // elems_per_flag if elems_per_flag else 0
