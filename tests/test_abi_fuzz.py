@@ -18,8 +18,8 @@ from hypothesis import strategies as st  # noqa: E402
 
 from collective_datapath_amd import binding as B  # noqa: E402
 
-if torch.cuda.is_available():
-    pytest.skip("valid calls would launch on fake addresses: CPU-only module", allow_module_level=True)
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="valid calls would launch on fake addresses: CPU-only module")
 
 BASE = 0x7F0000000000
 SPAN = 1 << 38            # far apart: no two slots overlap at any legal size
