@@ -456,6 +456,16 @@ def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
         check_linked_workspace(B, D, ws, i + 1)
 
 
+def test_twoshot_linked_first_call_inside_a_capture(B):
+    """A fresh process whose first linked call is captured in a graph."""
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "linked_capture_first.py")],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
+
+
 def test_twoshot_linked_empty_call_leaves_counters(B, D):
     ws = linked_workspace(B, 4, 0)
     B.pc_twoshot_linked([0] * 4, [0] * 4, 0, ws)
