@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="timed calls of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
-                    choices=["all", "headline", "c1", "c1v", "c2", "c2s", "c3", "c5", "atom_copy", "sweep",
+                    choices=["all", "headline", "c1", "c1v", "c2", "c2s", "c3", "c5", "atom_copy", "hbm", "sweep",
                              "sweep_cold", "copy"],
                     help="run one part only (profiling); 'copy' times a plain device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -397,6 +397,119 @@ def run_c3(d, B, synth, oracle, args, out):
     out["configs"]["twoshot_linked_1m"]["waits_abandoned"] = int(ws[B.PC_LINKED_STATUS_WORD])
 
 
+def run_hbm_regime(d, B, synth, oracle, args, out):
+    """Every other call at 8 ranks x 64 MiB (HBM-bound; event-timed back to
+    back).  Outputs are checked against the oracle at sampled positions, run
+    on the sampled inputs; ready bitmaps of all-current data must be full."""
+    torch = d.torch
+    n, k = 8, 32 << 20
+    g = torch.Generator(device=d.dev)
+    g.manual_seed(64)
+
+    def rnd(count, dtype=torch.int16):
+        return torch.randint(-32768, 32768, (count,), dtype=torch.int32, device=d.dev,
+                             generator=g).to(dtype)
+
+    def ev_us(fn, reps=20):
+        return d.events_ms(fn, reps, 3) * 1e3
+
+    idx_np = np.concatenate([np.arange(0, 4096), np.arange(k - 4096, k),
+                             np.random.default_rng(64).integers(0, k, 1 << 14)])
+    idx = torch.from_numpy(idx_np).to(d.dev)
+    ins = [rnd(k) for _ in range(n)]
+    xs = [d.down(t[idx], np.uint16) for t in ins]
+    want = oracle.reduce(xs) if oracle is not None else None
+    rows = {}
+
+    def row(name, nbytes, us, ok):
+        rows[name] = {"event_us_per_launch": round(us, 2), "bytes_per_call": nbytes,
+                      "gbs": round(gbs(nbytes, us), 1), "frac_of_hbm_peak": round(gbs(nbytes, us) / HBM_PEAK_GBS, 4)}
+        if oracle is not None:
+            out["parity"]["hbm_" + name] = bool(ok)
+
+    outs = [torch.empty(k, dtype=torch.int16, device=d.dev) for _ in range(n)]
+    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4, dtype=torch.int32, device=d.dev)
+    for name, fn, units in (("twoshot", lambda: B.pc_twoshot(ins, outs, k), 2 * n + 1),
+                            ("twoshot_fused", lambda: B.pc_twoshot_fused(ins, outs, k), 2 * n),
+                            ("twoshot_linked", lambda: B.pc_twoshot_linked(ins, outs, k, ws), 2 * n + 1)):
+        for o in outs:
+            o.fill_(-1)
+        us = ev_us(fn)
+        ok = want is not None and all(np.array_equal(d.down(o[idx], np.uint16), want) for o in outs)
+        row(name, units * 2 * k, us, ok)
+    del outs, ws
+    # LL: one rank packed (timed), then all ranks' lines consumed, all current.
+    lines = [torch.empty(k // 2, dtype=torch.int64, device=d.dev) for _ in range(n)]
+    for r in range(n):
+        B.pc_pack_ll(ins[r], lines[r], k, 7)
+    us = ev_us(lambda: B.pc_pack_ll(ins[0], lines[0], k, 7))
+    pairs = idx[idx % 2 == 0]
+    line_idx = pairs // 2
+    ok = oracle is not None and np.array_equal(
+        d.down(lines[0][line_idx], np.uint64),
+        oracle.pack_ll(np.stack([d.down(ins[0][pairs], np.uint16), d.down(ins[0][pairs + 1], np.uint16)], 1).reshape(-1), 7))
+    row("pack_ll", 6 * k, us, ok)
+    res = torch.full((k,), -1, dtype=torch.int16, device=d.dev)
+    bm = torch.empty(k // 128, dtype=torch.int64, device=d.dev)
+    us = ev_us(lambda: B.pc_consume_ll(lines, res, k, 7, bm))
+    ok = want is not None and np.array_equal(d.down(res[idx], np.uint16), want) and \
+        bool((bm == -1).all())
+    row("consume_ll", n * 4 * k + 2 * k + k // 16, us, ok)
+    del lines
+    # Sentinel: publish (timed alone), then publish-and-consume cycles; the
+    # consume time is the cycle minus its publishes.
+    slots = [torch.empty(k, dtype=torch.int16, device=d.dev) for _ in range(n)]
+    us = ev_us(lambda: B.pc_publish_sentinel(ins[0], slots[0], k))
+    pub = [d.down(slots[0][idx], np.uint16)]
+    ok = oracle is not None and np.array_equal(pub[0], oracle.publish_sentinel(xs[0]))
+    row("publish_sentinel", 4 * k, us, ok)
+    bms = torch.empty(k // 512, dtype=torch.int64, device=d.dev)
+
+    def publish_all():
+        for r in range(n):
+            B.pc_publish_sentinel(ins[r], slots[r], k)
+
+    def cycle():
+        publish_all()
+        B.pc_consume_sentinel(slots, res, k, bms)
+    us_publish = ev_us(publish_all, 10)
+    us = ev_us(cycle, 10) - us_publish             # the cycle runs last: slots end re-armed
+    ok = oracle is not None and np.array_equal(
+        d.down(res[idx], np.uint16), oracle.reduce([oracle.publish_sentinel(x) for x in xs])) and \
+        bool((bms == -1).all()) and bool((slots[n - 1][idx] == -1).all())
+    row("consume_sentinel", n * 2 * k + 2 * k + n * 2 * k + k // 64, us, ok)
+    del slots
+    # Speculative reduce, one flag per 8192 elements, all flags current.
+    flags = [torch.full((k // 8192,), 5, dtype=torch.int32, device=d.dev) for _ in range(n)]
+    att = torch.empty(k // 8192, dtype=torch.int32, device=d.dev)
+    res.fill_(-1)
+    us = ev_us(lambda: B.pc_reduce_validated(ins, flags, res, k, 8192, 5, 1, att))
+    ok = want is not None and np.array_equal(d.down(res[idx], np.uint16), want) and bool((att == 1).all())
+    row("reduce_validated", 9 * 2 * k + 4 * n * (k // 8192), us, ok)
+    del flags, att, res
+    # All-gather of 8 shards of 64 MiB payload, every record current.
+    sb = 2 * k
+    blocks = sb // 128
+    recs = []
+    for r in range(n):
+        rec = torch.empty(blocks * 17, dtype=torch.int64, device=d.dev)
+        rv = rec.view(blocks, 17)
+        rv[:, 0] = 7
+        rv[:, 1:] = rnd(blocks * 64).view(torch.int64).view(blocks, 16)
+        recs.append(rec)
+    agout = torch.empty(n * sb // 2, dtype=torch.int16, device=d.dev)
+    agbm = torch.empty(n * blocks // 64, dtype=torch.int64, device=d.dev)
+    us = ev_us(lambda: B.pc_allgather_copy(recs, agout, sb, 7, agbm))
+    sample = torch.from_numpy(np.random.default_rng(65).integers(0, blocks, 256)).to(d.dev)
+    ok = oracle is not None and bool((agbm == -1).all()) and all(
+        torch.equal(agout.view(n, blocks, 64)[r][sample].view(torch.int64), recs[r].view(blocks, 17)[sample][:, 1:])
+        for r in range(n))
+    row("allgather_copy", n * blocks * 136 + n * sb + n * blocks // 8, us, ok)
+    del recs, agout, agbm, ins
+    out["hbm_regime"] = {"workload": "8 ranks x 64 MiB per rank (LL: 128 MiB of lines per rank)", **rows}
+    torch.cuda.empty_cache()
+
+
 def run_copy_atom(d, B, synth, oracle, args, out):
     """The Atom copy: 256 MiB (HBM-bound, event-timed) and 1 MiB (per call
     in a graph, cache-resident).  Parity: the destination equals the source."""
@@ -564,7 +677,8 @@ def main():
     if args.only == "copy":
         run_copy(d, out, args.steps)
     for name, fn in (("c1", run_c1), ("c1v", run_c1v), ("c2", run_c2), ("c2s", run_c2s), ("c3", run_c3),
-                     ("c5", run_c5), ("atom_copy", run_copy_atom), ("sweep", run_sweep),
+                     ("c5", run_c5), ("atom_copy", run_copy_atom), ("hbm", run_hbm_regime),
+                     ("sweep", run_sweep),
                      ("sweep_cold", run_sweep_cold)):
         if args.only in ("all", name):
             log("running", name)
