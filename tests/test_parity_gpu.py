@@ -758,6 +758,60 @@ def test_twoshot_linked_next_to_a_persistent_kernel(B, D, orc):
                           orc.reduce([D.down(t[idx], np.uint16) for t in big]))
 
 
+def test_five_calls_on_five_streams(B, D, orc):
+    """Copy, LL consume, all-gather, speculative reduce and linked twoshot,
+    each on its own stream with its own buffers, launched together ten times:
+    the library keeps no shared state, so every result must be exact."""
+    n = 8
+    # copy
+    csrc = np.random.default_rng(90).integers(0, 256, 3 << 20, dtype=np.uint8)
+    c_in, c_out = D.up(csrc), torch.zeros(csrc.size, dtype=torch.uint8, device="cuda:0")
+    # LL consume (all current)
+    lk = 8 * 65536
+    lx = [synth.uniform_bf16(1900, 0, r, lk) for r in range(n)]
+    lines = [D.up(orc.pack_ll(x, 7)) for x in lx]
+    l_out = D.filled(lk, 0xFFFF)
+    l_bm = torch.empty(lk // 128, dtype=torch.int64, device="cuda:0")
+    # all-gather
+    ag = synth.GatherCase("streams", 1901, n, 8192 * 16, stale_frac=0.1)
+    recs, _ = ag.records()
+    shards = [D.up(r) for r in recs]
+    a_out = D.filled(n * ag.shard_bytes // 2, 0xFFFF)
+    a_bm = torch.empty(n * ag.blocks // 64, dtype=torch.int64, device="cuda:0")
+    # speculative reduce (all flags current)
+    vk = 8192 * 32
+    vx = [synth.uniform_bf16(1902, 0, r, vk) for r in range(n)]
+    v_in = [D.up(x) for x in vx]
+    v_flags = [torch.full((vk // 8192,), 11, dtype=torch.int32, device="cuda:0") for _ in range(n)]
+    v_out = D.filled(vk, 0xFFFF)
+    v_att = torch.empty(vk // 8192, dtype=torch.int32, device="cuda:0")
+    # linked twoshot
+    tk = 8 * 8 * 4096
+    tx = [synth.normal_bf16(1903, 0, r, tk) for r in range(n)]
+    t_in = [D.up(x) for x in tx]
+    t_out = [D.filled(tk, 0xFFFF) for _ in range(n)]
+    ws = linked_workspace(B, n, tk)
+    streams = [torch.cuda.Stream() for _ in range(5)]
+    torch.cuda.synchronize()
+    for _ in range(10):
+        B.pc_copy(c_out, c_in, csrc.size, stream=streams[0])
+        B.pc_consume_ll(lines, l_out, lk, 7, l_bm, stream=streams[1])
+        B.pc_allgather_copy(shards, a_out, ag.shard_bytes, ag.seq, a_bm, stream=streams[2])
+        B.pc_reduce_validated(v_in, v_flags, v_out, vk, 8192, 11, 4, v_att, stream=streams[3])
+        B.pc_twoshot_linked(t_in, t_out, tk, ws, stream=streams[4])
+    torch.cuda.synchronize()
+    assert np.array_equal(D.down(c_out, np.uint8), csrc)
+    wo, wb = orc.consume_ll([orc.pack_ll(x, 7) for x in lx], lk, 7)
+    assert np.array_equal(D.down(l_out, np.uint16), wo) and np.array_equal(D.down(l_bm, np.uint64), wb)
+    wo, wb = orc.allgather_copy(recs, ag.shard_bytes, ag.seq)
+    assert np.array_equal(D.down(a_out, np.uint16), wo) and np.array_equal(D.down(a_bm, np.uint64), wb)
+    assert np.array_equal(D.down(v_out, np.uint16), orc.reduce(vx))
+    assert np.all(D.down(v_att, np.uint32) == 1)
+    want = orc.reduce(tx)
+    assert all(np.array_equal(D.down(o, np.uint16), want) for o in t_out)
+    check_linked_workspace(B, D, ws, 10)
+
+
 def test_binding_rejects_bad_tensors_before_launch(B, D):
     k = 4096
     x = D.up(synth.uniform_bf16(1310, 0, 0, k))
