@@ -710,6 +710,61 @@ def test_graph_replays_match_oracle(B, D, orc):
             o.fill_(-1)                           # the next replay must rewrite them
 
 
+def test_graph_replays_of_the_other_calls(B, D, orc):
+    """Copy, two-launch twoshot, all-gather, sentinel publish + consume and the
+    speculative reduce captured once and replayed with new inputs written
+    eagerly between replays; every replay must equal the oracle."""
+    n, k = 8, 8 * 4096
+    ins = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
+    cp = torch.empty(k, dtype=torch.int16, device="cuda:0")
+    outs = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
+    slots = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
+    s_out = torch.empty(k, dtype=torch.int16, device="cuda:0")
+    s_bm = torch.empty(k // 512, dtype=torch.int64, device="cuda:0")
+    flags = [torch.full((k // 8192,), 3, dtype=torch.int32, device="cuda:0") for _ in range(n)]
+    v_out = torch.empty(k, dtype=torch.int16, device="cuda:0")
+    v_att = torch.empty(k // 8192, dtype=torch.int32, device="cuda:0")
+    ag = synth.GatherCase("graph", 1910, n, 8192 * 2)
+    rec_dev = [torch.empty(ag.blocks * 136, dtype=torch.uint8, device="cuda:0") for _ in range(n)]
+    a_out = torch.empty(n * ag.shard_bytes // 2, dtype=torch.int16, device="cuda:0")
+    a_bm = torch.empty(n * ag.blocks // 64, dtype=torch.int64, device="cuda:0")
+    for t in ins + rec_dev:
+        t.zero_()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            B.pc_copy(cp, ins[3], 2 * k)
+            B.pc_twoshot(ins, outs, k)
+            B.pc_allgather_copy(rec_dev, a_out, ag.shard_bytes, ag.seq, a_bm)
+            for r in range(n):
+                B.pc_publish_sentinel(ins[r], slots[r], k)
+            B.pc_consume_sentinel(slots, s_out, k, s_bm)
+            B.pc_reduce_validated(ins, flags, v_out, k, 8192, 3, 2, v_att)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xs = [synth.normal_bf16(1911 + rep, 0, r, k) for r in range(n)]
+        for t, x in zip(ins, xs):
+            t.copy_(D.up(x))
+        recs, _ = synth.GatherCase("graph", 1920 + rep, n, 8192 * 2).records()
+        for t, rc in zip(rec_dev, recs):
+            t.copy_(D.up(rc))
+        a_out.fill_(-1)            # blocks that are not ready keep what is there: 0xFFFF, as in the oracle
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = orc.reduce(xs)
+        assert np.array_equal(D.down(cp, np.uint16), xs[3]), rep
+        assert all(np.array_equal(D.down(o, np.uint16), want) for o in outs), rep
+        wo, wb = orc.allgather_copy(recs, ag.shard_bytes, ag.seq)
+        assert np.array_equal(D.down(a_out, np.uint16), wo) and np.array_equal(D.down(a_bm, np.uint64), wb), rep
+        assert np.array_equal(D.down(s_out, np.uint16), orc.reduce([orc.publish_sentinel(x) for x in xs])), rep
+        assert np.all(D.down(s_bm, np.uint64) == np.uint64(0xFFFFFFFFFFFFFFFF)), rep
+        assert all(np.all(D.down(sl, np.uint16) == 0xFFFF) for sl in slots), rep   # re-armed
+        assert np.array_equal(D.down(v_out, np.uint16), want) and np.all(D.down(v_att, np.uint32) == 1), rep
+
+
 def test_two_streams_disjoint_buffers(B, D, orc):
     n, k = 4, 8 * 65536
     xa = [synth.uniform_bf16(1300, 0, r, k) for r in range(n)]
