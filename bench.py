@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604518049,
+TRAFFIC = {"bytes": 604518010,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
            "sha256": "9139d9dfcc413259f4bff60b6fdd5b647aba32ad3153cfa0700f8004856d23a3"}
