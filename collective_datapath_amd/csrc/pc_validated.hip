@@ -11,14 +11,17 @@
 // with no ordering between them; the check is sound when ranks progress
 // monotonically (SiFAR, Section 8.1).
 //
-// Tile b (elems_per_flag elements, one workgroup of elems_per_flag / 8
-// lanes) is validated by flag word b of every rank.  The retry loop is
-// bounded by max_attempts so every kernel ends; attempts[b] receives the
-// attempt that validated (1-based) or 0.
+// Tile b (elems_per_flag elements) is validated by flag word b of every
+// rank.  Below a 64 MiB working set each tile has a workgroup of
+// elems_per_flag / 8 lanes; from there a persistent grid takes the tiles in
+// batches.  The retry loop is bounded by max_attempts so every kernel ends;
+// attempts[b] receives the attempt that validated (1-based) or 0.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 
 namespace pcdp {
+
+constexpr int kBlock = 256;
 
 // One attempt's reads.  The first attempt reads payload and flags the
 // default way, so they may come from the caches; a stale cached flag holds
@@ -93,6 +96,114 @@ __global__ __launch_bounds__(kLanes) void k_reduce_validated(Ptrs<const u32x4*> 
     if (t == 0) attempts[b] = accepted;
 }
 
+// Bandwidth regime (working sets of 64 MiB and more): a persistent grid of
+// two 256-lane workgroups per CU, the structure of the persistent reduce.
+// Workgroup w takes tiles w, w + grid, ... in batches of kBatch; lane t holds
+// chunks t, t + 256, ... (U = elems_per_flag / 2048 of them) of each tile.
+// Lane j < kBatch loads and folds the flags of the batch's tile j ahead of
+// the payload loads, as lane 0 does above.  The folded payload of the whole
+// batch waits in registers until a barrier, then every tile that passed the
+// check is stored (a failing tile gets a zero-length resource, so the stores
+// carry no branch).  A tile that failed then goes through the same bounded
+// retry as in the kernel above, one tile at a time.
+template <int N, int U>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
+void k_reduce_validated_persistent(Ptrs<const u32x4*> src, Ptrs<const uint32_t*> flags, u32x4* out,
+                                   uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
+                                   uint32_t ntiles) {
+    // Tiles per batch, from a sweep at 8 ranks x 64 MiB: 16 for one or two
+    // chunks per lane, 8 for four (32 chunks, as in the persistent reduce).
+    constexpr int kBatch = U == 4 ? 8 : 16;
+    constexpr uint32_t kTile = kBlock * U;
+    static_assert(kBatch <= 32, "one bit per tile of a batch");
+    __shared__ uint32_t passed_lds, again_lds;
+    const uint32_t t = threadIdx.x, stride = gridDim.x;
+    const uint32_t expect = (uint32_t)N * flag;
+    for (uint32_t g0 = blockIdx.x; g0 < ntiles; g0 += stride * kBatch) {
+        // The first wave checks the batch: bit j of `passed` is set iff tile
+        // j exists and its folded flags equal N * flag.
+        if (t < 64) {
+            bool ok = false;
+            const uint32_t g = g0 + t * stride;
+            if (t < (uint32_t)kBatch && g < ntiles) {
+                uint32_t f[N];
+                load_flags<N, __HIP_MEMORY_SCOPE_WORKGROUP>(f, flags, g);
+                ok = fold_flags<N>(f) == expect;
+            }
+            const uint64_t m = __ballot(ok);
+            if (t == 0) passed_lds = (uint32_t)m;
+        }
+        u32x4 o[kBatch][U];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            // A tile past the end gets a zero-length resource: its loads
+            // return zero and its stores are dropped.
+            const uint32_t g = g0 + j * stride;
+            const size_t first = g < ntiles ? (size_t)g * kTile : 0;
+            const uint32_t bytes = g < ntiles ? kTile * 16u : 0u;
+            u32x4 v[U][N];
+#pragma unroll
+            for (int r = 0; r < N; ++r) {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, bytes);
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u][r] = load16_tile(rs, (u * kBlock + t) * 16u);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) o[j][u] = fold_chunk<N>(v[u]);
+        }
+        __syncthreads();
+        // Read through readfirstlane, so the mask, the store resources and
+        // every branch on them stay scalar (a value read from LDS is taken as
+        // varying across lanes, which would put the resources in vector
+        // registers behind a loop over lanes).
+        const uint32_t passed = __builtin_amdgcn_readfirstlane(passed_lds);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const uint32_t g = g0 + j * stride;
+            const bool keep = g < ntiles && ((passed >> j) & 1u);
+            const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + (keep ? (size_t)g * kTile : 0),
+                                                        keep ? kTile * 16u : 0u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, o[j][u]);
+        }
+        if (t < (uint32_t)kBatch && g0 + t * stride < ntiles && ((passed >> t) & 1u)) attempts[g0 + t * stride] = 1;
+        // The rare path: retry each failing tile of the batch, one at a time.
+        // Every branch below is uniform for the workgroup.
+#pragma unroll 1
+        for (int j = 0; j < kBatch; ++j) {
+            const uint32_t g = g0 + j * stride;
+            if (g >= ntiles) break;
+            if ((passed >> j) & 1u) continue;
+            const size_t first = (size_t)g * kTile;
+            uint32_t accepted = 0;
+            for (uint32_t a = 2; a <= max_attempts; ++a) {
+                __syncthreads();  // every wave has read the previous verdict
+                uint32_t f[N] = {};
+                if (t == 0) load_flags<N, __HIP_MEMORY_SCOPE_AGENT>(f, flags, g);
+                u32x4 v[U][N];
+#pragma unroll
+                for (int r = 0; r < N; ++r) {
+                    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, kTile * 16u);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[u][r] = load16_rsrc<kPolicyDeviceScope>(rs, (u * kBlock + t) * 16u);
+                }
+                if (t == 0) again_lds = fold_flags<N>(f) == expect;
+                __syncthreads();
+                if (__builtin_amdgcn_readfirstlane(again_lds)) {
+                    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + first, kTile * 16u);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, fold_chunk<N>(v[u]));
+                    accepted = a;
+                    break;
+                }
+            }
+            if (t == 0) attempts[g] = accepted;
+        }
+        __syncthreads();  // passed_lds is rewritten by the next batch
+    }
+}
+
 template <int N, int kLanes>
 static hipError_t go_validated(Ptrs<const u32x4*> s, Ptrs<const uint32_t*> f, u32x4* out,
                                uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
@@ -115,6 +226,35 @@ static hipError_t go_validated_u(int u, Ptrs<const u32x4*> s, Ptrs<const uint32_
     }
 }
 
+template <int N, int U>
+static hipError_t go_validated_persistent(Ptrs<const u32x4*> s, Ptrs<const uint32_t*> f, u32x4* out,
+                                          uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
+                                          size_t tiles, hipStream_t stream) {
+    // Whole rounds of at most two workgroups per CU, then as few workgroups
+    // as give that many rounds.
+    uint32_t ntiles = (uint32_t)tiles;
+    const uint32_t slots = 2 * device_cus();
+    const uint32_t rounds = (ntiles + slots - 1) / slots;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    void* args[] = {&s, &f, &out, &flag, &max_attempts, &attempts, &ntiles};
+    return hipLaunchKernel((const void*)&k_reduce_validated_persistent<N, U>, dim3(grid), dim3(kBlock),
+                           args, 0, stream);
+}
+
+template <int N>
+static hipError_t go_validated_persistent_u(int u, Ptrs<const u32x4*> s, Ptrs<const uint32_t*> f,
+                                            u32x4* out, uint32_t flag, uint32_t max_attempts,
+                                            uint32_t* attempts, size_t tiles, hipStream_t stream) {
+    switch (u) {
+        case 1: return go_validated_persistent<N, 1>(s, f, out, flag, max_attempts, attempts, tiles, stream);
+        case 2: return go_validated_persistent<N, 2>(s, f, out, flag, max_attempts, attempts, tiles, stream);
+        case 4: return go_validated_persistent<N, 4>(s, f, out, flag, max_attempts, attempts, tiles, stream);
+        // Three chunks per lane spilled registers at every batch size tried
+        // (4x slower); that spacing keeps the one-tile-per-workgroup kernel.
+        default: return go_validated_u<N>(u, s, f, out, flag, max_attempts, attempts, tiles, stream);
+    }
+}
+
 hipError_t launch_reduce_validated(const void* const* src, const void* const* flags, int n,
                                    void* out, size_t k, size_t elems_per_flag, uint32_t flag,
                                    uint32_t max_attempts, void* attempts, hipStream_t stream) {
@@ -128,6 +268,19 @@ hipError_t launch_reduce_validated(const void* const* src, const void* const* fl
     uint32_t* at = static_cast<uint32_t*>(attempts);
     const int u = (int)(elems_per_flag / 2048);
     const size_t tiles = k / elems_per_flag;
+    if ((size_t)(n + 1) * k * 2 >= ((size_t)64 << 20)) {
+        switch (n) {
+            case 1: return go_validated_persistent_u<1>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 2: return go_validated_persistent_u<2>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 3: return go_validated_persistent_u<3>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 4: return go_validated_persistent_u<4>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 5: return go_validated_persistent_u<5>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 6: return go_validated_persistent_u<6>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 7: return go_validated_persistent_u<7>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            case 8: return go_validated_persistent_u<8>(u, s, f, o, flag, max_attempts, at, tiles, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (n) {
         case 1: return go_validated_u<1>(u, s, f, o, flag, max_attempts, at, tiles, stream);
         case 2: return go_validated_u<2>(u, s, f, o, flag, max_attempts, at, tiles, stream);

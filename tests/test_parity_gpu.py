@@ -657,6 +657,39 @@ def test_reduce_validated_in_place(B, D, orc):
     assert np.array_equal(D.down(ins[1], np.uint16), orc.reduce(xs))
 
 
+# Working sets of 64 MiB and more run on the persistent kernel (two workgroups
+# per CU taking batches of 16 or 8 tiles).  These tile counts leave the last
+# batch of most workgroups partly empty; 6144 elements per flag stays on the
+# one-tile-per-workgroup kernel at every size.  The flag's multiple wraps
+# mod 2^32, and a tenth of the tiles carry a stale flag on some rank.
+@pytest.mark.parametrize("n,t,tiles,in_place", [(8, 8192, 515, False), (8, 2048, 2053, False),
+                                                (8, 4096, 1030, False), (2, 4096, 2737, False),
+                                                (1, 8192, 2051, False), (5, 6144, 913, False),
+                                                (3, 2048, 4099, False), (6, 4096, 1173, False),
+                                                (7, 8192, 517, False), (4, 8192, 821, True)])
+def test_reduce_validated_bandwidth_regime(B, D, orc, n, t, tiles, in_place):
+    k = t * tiles
+    say("validated bandwidth regime", n, t, tiles, in_place)
+    assert (n + 1) * 2 * k >= 64 << 20
+    case = synth.ValidatedCase("vb", 95 + n, n, k, t, flag=0x9E3779B9, stale_frac=0.1)
+    xs, fl = case.payloads(), case.flags()
+    # A tile that never validates leaves out untouched: prefilled with
+    # 0xFFFF, or input 1 when the call runs in place.
+    start = xs[1].copy() if in_place else None
+    want_out, want_ok = orc.reduce_validated(xs, fl, t, case.flag, out=start)
+    assert 0 < int(want_ok.sum()) < tiles
+    if not in_place:
+        got_out, got_at = gpu_validated(B, D, xs, fl, t, case.flag, max_attempts=3)
+    else:
+        ins = [D.up(x) for x in xs]
+        dev_fl = [torch.from_numpy(f.view(np.int32)).to("cuda:0") for f in fl]
+        at = torch.full((tiles,), -1, dtype=torch.int32, device="cuda:0")
+        B.pc_reduce_validated(ins, dev_fl, ins[1], k, t, case.flag, 3, at)
+        got_out, got_at = D.down(ins[1], np.uint16), D.down(at, np.uint32)
+    assert np.array_equal(got_at, want_ok)              # static inputs: attempt 1 or never
+    assert np.array_equal(got_out, want_out)
+
+
 # ---- graph capture and concurrent streams ------------------------------------------------
 
 def test_graph_replays_match_oracle(B, D, orc):
