@@ -88,6 +88,106 @@ __global__ __launch_bounds__(W * kWave) void k_consume_ll(Ptrs<const u32x2*> lin
     }
 }
 
+// ---- consume, bandwidth regime (working sets of 512 MiB and more) -----------------
+// A persistent grid of two 256-lane workgroups per CU.  Tile g holds lines
+// [2048 g, 2048 g + 2048): wave w owns its groups 8w .. 8w + 7 of 64 lines,
+// and lane l line l of each group, as above.  Workgroup b takes tiles b,
+// b + grid, ... in batches of 8.  Every line of a batch is loaded (one
+// non-temporal 8-byte buffer load per line and rank, so data and sequence
+// number still arrive together), checked and folded into registers; after a
+// barrier the batch's results and bitmap words are stored.  A line that is
+// not ready gets an out-of-range store offset, which the tile's buffer
+// resource drops, so no store sits behind a branch.
+constexpr int kLLGroups = 8;                                     // per wave per tile
+constexpr uint32_t kLLTileLines = 4 * kWave * kLLGroups;         // 2048
+constexpr int kLLBatch = 8;                                      // tiles per batch
+constexpr uint32_t kDropOffset = 0x80000000u;                    // past every tile resource
+
+__device__ __forceinline__ u32x2 load8_nt(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, kPolicyNonTemporal));
+}
+
+// One batch: tiles g0, g0 + stride, ... (kBatch of them).  kAllValid: every
+// tile of the batch exists, so no tile needs a test; otherwise (a
+// workgroup's last batch) the missing tiles are skipped, so they issue no
+// loads at all.
+template <int N, int kBatch, bool kAllValid>
+__device__ __forceinline__ void consume_ll_batch(const Ptrs<const u32x2*>& lines, uint32_t* out,
+                                                 uint64_t* bitmap, uint32_t seq, size_t nlines,
+                                                 uint32_t ntiles, uint32_t g0, uint32_t stride) {
+    static_assert(kBatch * kLLGroups <= 64, "one readiness bit per line of a batch");
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t o[kBatch][kLLGroups];
+    uint64_t ready_bits = 0;  // bit j * kLLGroups + u: this lane's line of tile j, group u
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const uint32_t g = g0 + j * stride;
+        if (!kAllValid && g >= ntiles) continue;  // uniform for the workgroup
+        const size_t first = (size_t)g * kLLTileLines;
+        const size_t left = nlines - first;
+        const uint32_t nl = (uint32_t)(left < kLLTileLines ? left : kLLTileLines);
+        u32x2 l[kLLGroups][N];
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(lines.p[r] + first, nl * 8u);
+#pragma unroll
+            for (int u = 0; u < kLLGroups; ++u)
+                l[u][r] = load8_nt(rs, ((wave * kLLGroups + u) * kWave + lane) * 8u);
+        }
+#pragma unroll
+        for (int u = 0; u < kLLGroups; ++u) {
+            bool ready = true;
+            float lo = -0.0f, hi = -0.0f;
+#pragma unroll
+            for (int r = 0; r < N; ++r) {
+                ready &= l[u][r][1] == seq;  // no short circuit: no branch per rank
+                lo = lo + widen_lo(l[u][r][0]);
+                hi = hi + widen_hi(l[u][r][0]);
+            }
+            o[j][u] = narrow_pair(lo, hi);
+            ready_bits |= (uint64_t)ready << (j * kLLGroups + u);
+        }
+        // Keep the next tile's address and descriptor set-up behind this
+        // fold; computing all of them up front spilled registers.
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const uint32_t g = g0 + j * stride;
+        if (!kAllValid && g >= ntiles) continue;
+        const size_t first = (size_t)g * kLLTileLines;
+        const size_t left = nlines - first;
+        const uint32_t nl = (uint32_t)(left < kLLTileLines ? left : kLLTileLines);
+        const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + first, nl * 4u);
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(bitmap + first / kWave, nl / kWave * 8u);
+#pragma unroll
+        for (int u = 0; u < kLLGroups; ++u) {
+            const bool ready = (ready_bits >> (j * kLLGroups + u)) & 1u;
+            const uint32_t line = (wave * kLLGroups + u) * kWave + lane;
+            __builtin_amdgcn_raw_buffer_store_b32(o[j][u], ro, ready ? line * 4u : kDropOffset, 0,
+                                                  kPolicyDeviceScope);
+            const uint64_t word = __ballot(ready);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, word), rb,
+                                                  lane == 0 ? (wave * kLLGroups + u) * 8u : kDropOffset,
+                                                  0, kPolicyDeviceScope);
+        }
+    }
+}
+
+template <int N, int kBatch>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void k_consume_ll_persistent(Ptrs<const u32x2*> lines, uint32_t* out, uint64_t* bitmap, uint32_t seq,
+                             size_t nlines, uint32_t ntiles) {
+    const uint32_t stride = gridDim.x;
+    for (uint32_t g0 = blockIdx.x; g0 < ntiles; g0 += stride * kBatch) {
+        if (g0 + (kBatch - 1) * stride < ntiles)
+            consume_ll_batch<N, kBatch, true>(lines, out, bitmap, seq, nlines, ntiles, g0, stride);
+        else
+            consume_ll_batch<N, kBatch, false>(lines, out, bitmap, seq, nlines, ntiles, g0, stride);
+    }
+}
+
 // Bytes per rank below which the one-wave shapes are used.
 constexpr size_t kSmallBytes = (size_t)4 << 20;
 
@@ -117,9 +217,29 @@ static hipError_t go_consume_shape(Ptrs<const u32x2*> p, uint32_t* out, uint64_t
                            stream);
 }
 
+template <int N, int kBatch>
+static hipError_t go_consume_persistent(Ptrs<const u32x2*> p, uint32_t* out, uint64_t* bitmap,
+                                        uint32_t seq, size_t nlines, hipStream_t stream) {
+    // Whole rounds of at most two workgroups per CU, then as few workgroups
+    // as give that many rounds.
+    uint32_t ntiles = (uint32_t)((nlines + kLLTileLines - 1) / kLLTileLines);
+    const uint32_t slots = 2 * device_cus();
+    const uint32_t rounds = (ntiles + slots - 1) / slots;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    void* args[] = {&p, &out, &bitmap, &seq, &nlines, &ntiles};
+    return hipLaunchKernel((const void*)&k_consume_ll_persistent<N, kBatch>, dim3(grid), dim3(4 * kWave),
+                           args, 0, stream);
+}
+
 template <int N>
 static hipError_t go_consume(Ptrs<const u32x2*> p, uint32_t* out, uint64_t* bitmap, uint32_t seq,
                              size_t nlines, hipStream_t stream) {
+    // Lines read plus results written.  From 512 MiB, twice the last-level
+    // cache, the persistent kernel is ahead (8 ranks: 172 vs 207 us at 64 MiB
+    // per rank, 88 vs 102 at 32 MiB); below it, the kernel above keeps more
+    // of its inputs in the cache between calls (44 vs 46 us at 16 MiB).
+    if (nlines * (8 * (size_t)N + 4) >= ((size_t)512 << 20))
+        return go_consume_persistent<N, kLLBatch>(p, out, bitmap, seq, nlines, stream);
     // Below 4 MiB per rank: two waves per workgroup (1.85 vs 1.91 us per
     // call at 8 ranks x 128 KiB; one, eight and sixteen waves were slower).
     if (nlines * 4 < kSmallBytes)

@@ -312,6 +312,32 @@ def test_consume_ll_shapes(B, D, orc, n, k):
     assert np.array_equal(got_out, want_out)
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_consume_ll_bandwidth_regime(B, D, orc, n):
+    # From 512 MiB of lines read plus results written the consumer is the
+    # persistent kernel.  Five 64-line groups past that size leave a ragged
+    # last 2048-line tile; ranks 0, 3 and 6 carry about 2% lines of the
+    # previous call (the stale payload packed with the stale sequence number).
+    nl = (-(-(512 << 20) // (8 * n + 4)) // 64 + 5) * 64
+    k = 2 * nl
+    say("consume_ll bandwidth regime", n, k)
+    pick = np.random.default_rng(800 + n)
+    staged = []
+    for r in range(n):
+        lines = orc.pack_ll(synth.uniform_bf16(800 + n, 0, r, k), synth.SEQ_CURRENT)
+        if r % 3 == 0:
+            idx = np.flatnonzero(pick.random(nl) < 0.02)
+            stale = orc.pack_ll(synth.uniform_bf16(800 + n, 1, r, k, 2.0, 3.0), synth.SEQ_STALE)
+            lines[idx] = stale[idx]
+        staged.append(lines)
+    want_out, want_bm = orc.consume_ll(staged, k, synth.SEQ_CURRENT)
+    got_out, got_bm = gpu_consume(B, D, [D.up(s) for s in staged], k, synth.SEQ_CURRENT)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+    del staged
+    torch.cuda.empty_cache()
+
+
 def test_consume_ll_one_rank_identity_all_patterns(B, D, orc):
     allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     lines = gpu_pack(B, D, allh, 9)
