@@ -73,7 +73,7 @@ __global__ __launch_bounds__(W * kWave) void k_consume_ll(Ptrs<const u32x2*> lin
         if (g >= nlines) break;
         bool ready = true;
 #pragma unroll
-        for (int r = 0; r < N; ++r) ready = ready && (l[u][r][1] == seq);
+        for (int r = 0; r < N; ++r) ready &= l[u][r][1] == seq;
         const uint64_t word = __ballot(ready);
         if (ready) {
             float lo = -0.0f, hi = -0.0f;

@@ -24,9 +24,11 @@ namespace pcdp {
 constexpr size_t kSentinelSmallBytes = (size_t)4 << 20;
 constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // two sentinel elements
 
-// 1 if neither bf16 half of `w` is the sentinel.
+// 1 if neither bf16 half of `w` is the sentinel.  Bitwise, not short
+// circuit: the readiness test of a pack combines 4 * N of these, and a
+// short-circuit chain compiled to a branch per term.
 __device__ __forceinline__ bool no_sentinel(uint32_t w) {
-    return (w & 0xFFFFu) != 0xFFFFu && (w >> 16) != 0xFFFFu;
+    return ((w & 0xFFFFu) != 0xFFFFu) & ((w >> 16) != 0xFFFFu);
 }
 
 // Replace each sentinel half of `w` by the canonical quiet NaN.
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(W * kWave) void k_consume_sentinel(Ptrs<u32x4*> slo
 #pragma unroll
         for (int r = 0; r < N; ++r)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ready = ready && no_sentinel(v[u][r][e]);
+            for (int e = 0; e < 4; ++e) ready &= no_sentinel(v[u][r][e]);
         const uint64_t word = __ballot(ready);
         if (ready) {
             out[g + lane] = fold_chunk<N>(v[u]);
