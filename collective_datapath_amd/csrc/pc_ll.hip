@@ -127,6 +127,7 @@ __device__ __forceinline__ void consume_ll_batch(const Ptrs<const u32x2*>& lines
         const size_t left = nlines - first;
         const uint32_t nl = (uint32_t)(left < kLLTileLines ? left : kLLTileLines);
         u32x2 l[kLLGroups][N];
+        uint32_t words_lo = 0, words_hi = 0;
 #pragma unroll
         for (int r = 0; r < N; ++r) {
             const __amdgpu_buffer_rsrc_t rs = tile_rsrc(lines.p[r] + first, nl * 8u);
@@ -146,7 +147,21 @@ __device__ __forceinline__ void consume_ll_batch(const Ptrs<const u32x2*>& lines
             }
             o[j][u] = narrow_pair(lo, hi);
             ready_bits |= (uint64_t)ready << (j * kLLGroups + u);
+            // Lane u of `words` takes the group's bitmap word.
+            const uint64_t word = __ballot(ready);
+            words_lo = lane == (uint32_t)u ? (uint32_t)word : words_lo;
+            words_hi = lane == (uint32_t)u ? (uint32_t)(word >> 32) : words_hi;
         }
+        // The wave's words leave in one 64-byte store by lanes 0..7 (one
+        // store per word wrote about four times the bitmap's bytes to HBM).
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(bitmap + first / kWave, nl / kWave * 8u);
+        u32x2 words;
+        words[0] = words_lo;
+        words[1] = words_hi;
+        __builtin_amdgcn_raw_buffer_store_b64(words, rb,
+                                              lane < (uint32_t)kLLGroups ? (wave * kLLGroups + lane) * 8u
+                                                                         : kDropOffset,
+                                              0, kPolicyDeviceScope);
         // Keep the next tile's address and descriptor set-up behind this
         // fold; computing all of them up front spilled registers.
         __builtin_amdgcn_sched_barrier(0);
@@ -160,17 +175,12 @@ __device__ __forceinline__ void consume_ll_batch(const Ptrs<const u32x2*>& lines
         const size_t left = nlines - first;
         const uint32_t nl = (uint32_t)(left < kLLTileLines ? left : kLLTileLines);
         const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + first, nl * 4u);
-        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(bitmap + first / kWave, nl / kWave * 8u);
 #pragma unroll
         for (int u = 0; u < kLLGroups; ++u) {
             const bool ready = (ready_bits >> (j * kLLGroups + u)) & 1u;
             const uint32_t line = (wave * kLLGroups + u) * kWave + lane;
             __builtin_amdgcn_raw_buffer_store_b32(o[j][u], ro, ready ? line * 4u : kDropOffset, 0,
                                                   kPolicyDeviceScope);
-            const uint64_t word = __ballot(ready);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, word), rb,
-                                                  lane == 0 ? (wave * kLLGroups + u) * 8u : kDropOffset,
-                                                  0, kPolicyDeviceScope);
         }
     }
 }
