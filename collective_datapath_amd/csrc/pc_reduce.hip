@@ -176,7 +176,9 @@ void k_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nsli
 // the ragged last tile, and the owner's own range gets a zero-length
 // resource, so a lane's N-1 stores issue back to back with no branch (a
 // branch per destination made each store wait for the one before it).
-template <int N, int U>
+// kStorePolicy: the copies' cache policy (default, or non-temporal once the
+// outputs are far larger than the last-level cache).
+template <int N, int U, int kStorePolicy>
 __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t nslice) {
     constexpr uint32_t kTile = kBlock * U;
     const uint32_t s = blockIdx.y;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t 
     for (int r = 0; r < N; ++r) {
         const __amdgpu_buffer_rsrc_t rd = tile_rsrc(outs.p[r] + first, (uint32_t)r == s ? 0u : bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u) store16_rsrc<0>(rd, (u * kBlock + t) * 16u, v[u]);
+        for (int u = 0; u < U; ++u) store16_rsrc<kStorePolicy>(rd, (u * kBlock + t) * 16u, v[u]);
     }
 }
 
@@ -282,17 +284,23 @@ static hipError_t dispatch_reduce(int n, Regime rg, Ptrs<const u32x4*> src, Ptrs
     }
 }
 
+// From 48 MiB per rank, where the two policies are level at 8 ranks, the
+// copies carry the non-temporal hint: 181 vs 192 us at 64 MiB per rank and
+// 269 vs 310 us at 96 MiB.  Below it the default policy is faster (87 vs
+// 92 us at 32 MiB), because the copies still find room in the caches.
+constexpr size_t kCopyoutStreamBytes = (size_t)48 << 20;
+
 template <int N>
 static hipError_t go_copyout(Ptrs<u32x4*> outs, uint32_t nslice, uint32_t slices, bool wide,
-                             hipStream_t stream) {
+                             bool nt, hipStream_t stream) {
+    void* args[] = {&outs, &nslice};
     if (wide) {
         dim3 grid((nslice + 2 * kBlock - 1) / (2 * kBlock), slices);
-        void* args[] = {&outs, &nslice};
-        return hipLaunchKernel((const void*)&k_copyout<N, 2>, grid, dim3(kBlock), args, 0, stream);
+        const void* k = nt ? (const void*)&k_copyout<N, 2, kPolicyNonTemporal> : (const void*)&k_copyout<N, 2, 0>;
+        return hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream);
     }
     dim3 grid((nslice + kBlock - 1) / kBlock, slices);
-    void* args[] = {&outs, &nslice};
-    return hipLaunchKernel((const void*)&k_copyout<N, 1>, grid, dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel((const void*)&k_copyout<N, 1, 0>, grid, dim3(kBlock), args, 0, stream);
 }
 
 static void fill_src(Ptrs<const u32x4*>& p, const void* const* src, int n) {
@@ -321,14 +329,15 @@ hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size
         dispatch_reduce<Out::kOwner>(n, rg, s, d, (uint32_t)nchunks_slice, (uint32_t)n, stream);
     if (e != hipSuccess || n == 1) return e;
     const bool wide = rg != Regime::kSmall;
+    const bool nt = per_rank * 16 >= kCopyoutStreamBytes;
     switch (n) {
-        case 2: return go_copyout<2>(d, (uint32_t)nchunks_slice, n, wide, stream);
-        case 3: return go_copyout<3>(d, (uint32_t)nchunks_slice, n, wide, stream);
-        case 4: return go_copyout<4>(d, (uint32_t)nchunks_slice, n, wide, stream);
-        case 5: return go_copyout<5>(d, (uint32_t)nchunks_slice, n, wide, stream);
-        case 6: return go_copyout<6>(d, (uint32_t)nchunks_slice, n, wide, stream);
-        case 7: return go_copyout<7>(d, (uint32_t)nchunks_slice, n, wide, stream);
-        case 8: return go_copyout<8>(d, (uint32_t)nchunks_slice, n, wide, stream);
+        case 2: return go_copyout<2>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
+        case 3: return go_copyout<3>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
+        case 4: return go_copyout<4>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
+        case 5: return go_copyout<5>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
+        case 6: return go_copyout<6>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
+        case 7: return go_copyout<7>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
+        case 8: return go_copyout<8>(d, (uint32_t)nchunks_slice, n, wide, nt, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -431,6 +431,20 @@ def test_twoshot_shapes(B, D, orc, n, slice_chunks, mode):
         assert np.array_equal(g, want)
 
 
+# From 48 MiB per rank the copy-out of the two-launch form writes with the
+# non-temporal hint; just below and past that size, with ragged slices.
+@pytest.mark.parametrize("n,per_rank_mib,extra", [(8, 48, 3), (8, 47, 5), (2, 50, 1), (5, 64, 7)])
+def test_twoshot_copyout_nontemporal(B, D, orc, n, per_rank_mib, extra):
+    sc = (per_rank_mib << 20) // (16 * n) + extra       # chunks per slice
+    k = 8 * n * sc
+    say("twoshot nt copy-out", n, k)
+    xs = [synth.normal_bf16(1700 + n, 0, r, k) for r in range(n)]
+    want = orc.reduce(xs, threads=THREADS)
+    for g in gpu_twoshot(B, D, xs, "two"):
+        assert np.array_equal(g, want)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode", TWOSHOT_MODES)
 def test_twoshot_in_place(B, D, orc, mode):
     n, k = 4, 8 * 4 * 999
