@@ -687,6 +687,50 @@ def test_reduce_validated_flags_fold_and_wrap(B, D, orc):
     assert list(got_at) == [1]
 
 
+def test_reduce_validated_concurrent_arrival(B, D, orc):
+    """A rank's flags arrive while the call is retrying: a kernel on a second
+    stream rewrites them after a bounded spin.  Retries re-read flags and
+    payload past the caches, so every tile validates once the rewrite is
+    visible, with the oracle's result; validating after the first attempt
+    shows the retry path at work.  All tiles validating at once means the
+    rewrite came first (skipped: nothing exercised).  Every tile giving up is
+    a failure if the rewrite finished well before the call did (the retries
+    then read stale data), and otherwise means the streams did not overlap
+    (skipped).  A mix of tiles that gave up and tiles that validated fails."""
+    n, epf, tiles, flag = 8, 2048, 64, 41
+    k = epf * tiles
+    xs = [synth.uniform_bf16(97, 0, r, k) for r in range(n)]
+    ins = [D.up(x) for x in xs]
+    fl = [torch.full((tiles,), flag, dtype=torch.int32, device="cuda:0") for _ in range(n)]
+    fl[3].fill_(flag - 1)                                   # rank 3 has not arrived
+    out = D.filled(k, 0xFFFF)
+    at = torch.full((tiles,), -1, dtype=torch.int32, device="cuda:0")
+    side = torch.cuda.Stream()
+    done_call = torch.cuda.Event(enable_timing=True)
+    done_flags = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    B.pc_reduce_validated(ins, fl, out, k, epf, flag, 65536, at)
+    done_call.record()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(100000)
+        fl[3].fill_(flag)
+        done_flags.record()
+    torch.cuda.synchronize()
+    lead_ms = done_flags.elapsed_time(done_call)             # > 0: the rewrite finished first
+    got_at = D.down(at, np.uint32)
+    got = D.down(out, np.uint16)
+    say("concurrent arrival: attempts", int(got_at.min()), "to", int(got_at.max()),
+        "; rewrite finished", round(lead_ms, 4), "ms before the call")
+    if np.all(got_at == 0):
+        assert lead_ms < 5.0, "flags rewritten long before the call ended, but no tile validated"
+        assert np.all(got == 0xFFFF)
+        pytest.skip("the call gave up before the rewrite: the streams did not overlap")
+    assert np.all(got_at >= 1), np.unique(got_at)
+    assert np.array_equal(got, orc.reduce(xs))
+    if np.all(got_at == 1):
+        pytest.skip("the rewrite came before the call's first read: no retry was needed")
+
+
 def test_reduce_validated_in_place(B, D, orc):
     n, t = 4, 4096
     xs = [synth.uniform_bf16(91, 0, r, 4 * t) for r in range(n)]
