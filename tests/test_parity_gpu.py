@@ -338,6 +338,47 @@ def test_consume_ll_bandwidth_regime(B, D, orc, n):
     torch.cuda.empty_cache()
 
 
+def test_consume_ll_lines_not_torn_under_concurrent_pack(B, D, orc):
+    """The LL protocol needs a line's data and sequence number to be observed
+    together.  A side stream rewrites 2M lines 64 times, alternating between
+    two payloads with their own sequence numbers, while the main stream
+    consumes them 32 times into separate outputs.  Every line a consume marks
+    ready must hold that version's payload (the oracle's fold of it, one
+    rank); every other line keeps the prefill.  Consumes that saw part of a
+    rewrite show the race was exercised; if none did, the test is skipped."""
+    k = 1 << 22
+    nl = k // 2
+    seqs = (5, 6)
+    pays = [synth.uniform_bf16(1900, v, 0, k) for v in range(2)]
+    want = [orc.reduce([p]).reshape(-1, 2) for p in pays]
+    src = [D.up(p) for p in pays]
+    lines = torch.empty(nl, dtype=torch.int64, device="cuda:0")
+    B.pc_pack_ll(src[0], lines, k, seqs[0])
+    calls = 32
+    outs = [D.filled(k, 0xFFFF) for _ in range(calls)]
+    bms = [torch.full((nl // 64,), -1, dtype=torch.int64, device="cuda:0") for _ in range(calls)]
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for i in range(2 * calls):
+        v = (i + 1) % 2
+        B.pc_pack_ll(src[v], lines, k, seqs[v], stream=side)
+        if i % 2 == 0:
+            j = i // 2
+            B.pc_consume_ll([lines], outs[j], k, seqs[j % 2], bms[j])
+    torch.cuda.synchronize()
+    partial = 0
+    for j in range(calls):
+        bm = D.down(bms[j], np.uint64)
+        ready = np.unpackbits(bm.view(np.uint8), bitorder="little").astype(bool)  # bit l of word w: line 64w + l
+        got = D.down(outs[j], np.uint16).reshape(-1, 2)
+        assert np.array_equal(got[ready], want[j % 2][ready]), j
+        assert np.all(got[~ready] == 0xFFFF), j
+        partial += int(0 < ready.sum() < nl)
+    say("concurrent pack: consumes that saw part of a rewrite", partial, "of", calls)
+    if partial == 0:
+        pytest.skip("no consume overlapped a rewrite")
+
+
 def test_consume_ll_one_rank_identity_all_patterns(B, D, orc):
     allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     lines = gpu_pack(B, D, allh, 9)
