@@ -472,17 +472,19 @@ def test_twoshot_shapes(B, D, orc, n, slice_chunks, mode):
         assert np.array_equal(g, want)
 
 
-# From 48 MiB per rank the copy-out of the two-launch form writes with the
-# non-temporal hint; just below and past that size, with ragged slices.
+# From 48 MiB per rank the copies of the two-launch and the flag-linked forms
+# carry the non-temporal hint; just below and past that size, with ragged
+# slices.
 @pytest.mark.parametrize("n,per_rank_mib,extra", [(8, 48, 3), (8, 47, 5), (2, 50, 1), (5, 64, 7)])
-def test_twoshot_copyout_nontemporal(B, D, orc, n, per_rank_mib, extra):
+def test_twoshot_copies_nontemporal(B, D, orc, n, per_rank_mib, extra):
     sc = (per_rank_mib << 20) // (16 * n) + extra       # chunks per slice
     k = 8 * n * sc
-    say("twoshot nt copy-out", n, k)
+    say("twoshot nt copies", n, k)
     xs = [synth.normal_bf16(1700 + n, 0, r, k) for r in range(n)]
     want = orc.reduce(xs, threads=THREADS)
-    for g in gpu_twoshot(B, D, xs, "two"):
-        assert np.array_equal(g, want)
+    for mode in ("two", "linked"):
+        for g in gpu_twoshot(B, D, xs, mode):
+            assert np.array_equal(g, want), mode
     torch.cuda.empty_cache()
 
 
