@@ -36,6 +36,7 @@ constexpr int kStageLoads = (kGroupPieces + kGBlock - 1) / kGBlock;  // 3 per la
 // non-temporal hint: the gathered output is written once here and read by a
 // later operation, and keeping it from displacing the shards in the caches
 // measured 22% faster on the 8 x 2 MiB workload.
+template <int kLoadPolicy>
 __global__ __launch_bounds__(kGBlock) void k_allgather(Ptrs<const u32x4*> shards, u32x4* out,
                                                         uint64_t* bitmap, uint64_t seq,
                                                         uint32_t groups) {
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(kGBlock) void k_allgather(Ptrs<const u32x4*> shards
         tile_rsrc(shards.p[r] + (size_t)g * kGroupPieces, kGroupPieces * 16u);
     u32x4 v[kStageLoads];
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) v[j] = load16_rsrc<0>(rs, (j * kGBlock + t) * 16u);
+    for (int j = 0; j < kStageLoads; ++j) v[j] = load16_rsrc<kLoadPolicy>(rs, (j * kGBlock + t) * 16u);
 #pragma unroll
     for (int j = 0; j < kStageLoads; ++j) __builtin_memcpy(&tile[2 * (j * kGBlock + t)], &v[j], sizeof v[j]);
     __syncthreads();
@@ -82,7 +83,15 @@ hipError_t launch_allgather(const void* const* shards, int n, void* out, size_t 
     uint32_t gr = (uint32_t)groups;
     dim3 grid(gr, (unsigned)n);
     void* args[] = {&p, &o, &b, &seq, &gr};
-    return hipLaunchKernel((const void*)&k_allgather, grid, dim3(kGBlock), args, 0, stream);
+    // Records read plus payloads written.  From 768 MiB, three times the
+    // last-level cache, the staging loads carry the non-temporal hint: at 8
+    // ranks 126 vs 138 us with 48 MiB shards, 169 vs 184 with 64 MiB and 257
+    // vs 277 with 96 MiB.  At 528 MiB (8 x 32 or 4 x 64 MiB) it cost 10%,
+    // and at 8 x 2 MiB it made the call 45% slower.
+    const size_t moved = (size_t)n * groups * kGroup * (kRecBytes + 128);
+    const void* k = moved >= ((size_t)768 << 20) ? (const void*)&k_allgather<kPolicyNonTemporal>
+                                                 : (const void*)&k_allgather<0>;
+    return hipLaunchKernel(k, grid, dim3(kGBlock), args, 0, stream);
 }
 
 }  // namespace pcdp

@@ -576,9 +576,16 @@ def test_allgather_2m_stale(B, D, orc):
     assert int(np.unpackbits(got_bm.view(np.uint8)).sum()) == 131072 - 8 * 1638
 
 
+# The last two move 768 MiB or more (records read plus payloads written),
+# where the staging loads carry the non-temporal hint; the one before sits
+# just below that.
 @pytest.mark.parametrize("n,shard_bytes,frac", [(1, 8192, 0.5), (3, 8192 * 3, 0.1),
-                                                 (8, 8192 * 17, 0.0), (2, 8192 * 5, 1.0)])
+                                                 (8, 8192 * 17, 0.0), (2, 8192 * 5, 1.0),
+                                                 (8, (46 << 20) + 8192 * 7, 0.1),
+                                                 (8, (47 << 20) + 8192 * 3, 0.1),
+                                                 (3, (125 << 20) + 8192 * 5, 0.05)])
 def test_allgather_shapes(B, D, orc, n, shard_bytes, frac):
+    say("allgather", n, shard_bytes)
     case = synth.GatherCase("shape", 1000 + n, n, shard_bytes, stale_frac=frac)
     recs, _ = case.records()
     want_out, want_bm = orc.allgather_copy(recs, shard_bytes, case.seq)
