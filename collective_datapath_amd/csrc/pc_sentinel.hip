@@ -96,6 +96,134 @@ __global__ __launch_bounds__(W * kWave) void k_consume_sentinel(Ptrs<u32x4*> slo
     }
 }
 
+// ---- consume in two passes, from 768 MiB moved ----------------------------------------
+// Pass 1 is the fold of the persistent LL consumer for packs: a persistent
+// grid of two 256-lane workgroups per CU, tile g = packs [P g, P g + P) with
+// P = 256 * kSFGroups; a batch's packs are loaded (non-temporal), checked
+// and folded into registers, each wave's bitmap words of a tile leave in one
+// store, and after a barrier the batch's ready results are stored (a pack
+// that is not ready gets an out-of-range offset, which the resource drops).
+// Pass 2 re-arms: workgroup (x, r) takes 1024 packs of slot r and writes the
+// sentinel over the ones pass 1 marked ready (non-temporal stores: the slots
+// are next written by their producers), so the slots are written one after
+// another rather than as N streams interleaved with the reads.  The two
+// passes are ordered by the stream; no pack is re-armed before its value is
+// captured.
+constexpr int kSFGroups = 2;                                  // per wave per tile
+constexpr uint32_t kSFTilePacks = 4 * kWave * kSFGroups;
+constexpr int kSFBatch = 8;                                   // tiles per batch
+constexpr uint32_t kSDrop = 0x80000000u;                      // past every tile resource
+
+template <int N, int kBatch, bool kAllValid>
+__device__ __forceinline__ void sentinel_fold_batch(const Ptrs<u32x4*>& slots, u32x4* out,
+                                                    uint64_t* bitmap, size_t npacks, uint32_t ntiles,
+                                                    uint32_t g0, uint32_t stride) {
+    static_assert(kBatch * kSFGroups <= 64, "one readiness bit per pack of a batch");
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    u32x4 o[kBatch][kSFGroups];
+    uint64_t ready_bits = 0;  // bit j * kSFGroups + u: this lane's pack of tile j, group u
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const uint32_t g = g0 + j * stride;
+        if (!kAllValid && g >= ntiles) continue;  // uniform for the workgroup
+        const size_t first = (size_t)g * kSFTilePacks;
+        const size_t left = npacks - first;
+        const uint32_t np = (uint32_t)(left < kSFTilePacks ? left : kSFTilePacks);
+        u32x4 v[kSFGroups][N];
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(slots.p[r] + first, np * 16u);
+#pragma unroll
+            for (int u = 0; u < kSFGroups; ++u)
+                v[u][r] = load16_rsrc<kPolicyNonTemporal>(rs, ((wave * kSFGroups + u) * kWave + lane) * 16u);
+        }
+        uint32_t words_lo = 0, words_hi = 0;  // lane u < kSFGroups: the bitmap word of group u
+#pragma unroll
+        for (int u = 0; u < kSFGroups; ++u) {
+            bool ready = true;
+#pragma unroll
+            for (int r = 0; r < N; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ready &= no_sentinel(v[u][r][e]);
+            o[j][u] = fold_chunk<N>(v[u]);
+            ready_bits |= (uint64_t)ready << (j * kSFGroups + u);
+            const uint64_t word = __ballot(ready);
+            words_lo = lane == (uint32_t)u ? (uint32_t)word : words_lo;
+            words_hi = lane == (uint32_t)u ? (uint32_t)(word >> 32) : words_hi;
+        }
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(bitmap + first / kWave, np / kWave * 8u);
+        u32x2 words;
+        words[0] = words_lo;
+        words[1] = words_hi;
+        __builtin_amdgcn_raw_buffer_store_b64(words, rb,
+                                              lane < (uint32_t)kSFGroups ? (wave * kSFGroups + lane) * 8u : kSDrop,
+                                              0, kPolicyDeviceScope);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next tile's set-up behind this fold
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const uint32_t g = g0 + j * stride;
+        if (!kAllValid && g >= ntiles) continue;
+        const size_t first = (size_t)g * kSFTilePacks;
+        const size_t left = npacks - first;
+        const uint32_t np = (uint32_t)(left < kSFTilePacks ? left : kSFTilePacks);
+        const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + first, np * 16u);
+#pragma unroll
+        for (int u = 0; u < kSFGroups; ++u) {
+            const bool ready = (ready_bits >> (j * kSFGroups + u)) & 1u;
+            store16_rsrc<kPolicyDeviceScope>(ro, ready ? ((wave * kSFGroups + u) * kWave + lane) * 16u : kSDrop,
+                                             o[j][u]);
+        }
+    }
+}
+
+template <int N, int kBatch>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void k_sentinel_fold_persistent(Ptrs<u32x4*> slots, u32x4* out, uint64_t* bitmap, size_t npacks,
+                                uint32_t ntiles) {
+    const uint32_t stride = gridDim.x;
+    for (uint32_t g0 = blockIdx.x; g0 < ntiles; g0 += stride * kBatch) {
+        if (g0 + (kBatch - 1) * stride < ntiles)
+            sentinel_fold_batch<N, kBatch, true>(slots, out, bitmap, npacks, ntiles, g0, stride);
+        else
+            sentinel_fold_batch<N, kBatch, false>(slots, out, bitmap, npacks, ntiles, g0, stride);
+    }
+}
+
+// Pass 2.  Grid: x = block of 1024 packs, y = slot r.  A wave's 64 lanes
+// share one bitmap word per group; tile-sized resources clamp the ragged
+// last block (its missing words read as zero, so nothing past the end is
+// written).
+constexpr int kRearmGroups = 4;  // 64-pack groups per wave
+template <int kPolicy>
+__global__ __launch_bounds__(4 * kWave) void k_sentinel_rearm(Ptrs<u32x4*> slots, const uint64_t* bitmap,
+                                                               size_t npacks) {
+    constexpr uint32_t kBlockPacks = 4 * kWave * kRearmGroups;
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const size_t first = (size_t)blockIdx.x * kBlockPacks;
+    const size_t left = npacks - first;
+    const uint32_t np = (uint32_t)(left < kBlockPacks ? left : kBlockPacks);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc(bitmap + first / kWave, np / kWave * 8u);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(slots.p[blockIdx.y] + first, np * 16u);
+    const u32x4 armed = {kSentinelWord, kSentinelWord, kSentinelWord, kSentinelWord};
+    uint32_t words[kRearmGroups][2];
+#pragma unroll
+    for (int u = 0; u < kRearmGroups; ++u) {
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+            rb, (wave * kRearmGroups + u) * 8u, 0, 0));
+        words[u][0] = w[0];
+        words[u][1] = w[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kRearmGroups; ++u) {
+        const uint32_t half = lane < 32 ? words[u][0] : words[u][1];
+        const bool ready = (half >> (lane & 31)) & 1u;
+        const uint32_t pack = (wave * kRearmGroups + u) * kWave + lane;
+        store16_rsrc<kPolicy>(rs, ready ? pack * 16u : kSDrop, armed);
+    }
+}
+
 template <int W, int U>
 static hipError_t go_publish(const u32x4* s, u32x4* d, size_t nchunks, hipStream_t stream) {
     const size_t tile = (size_t)W * kWave * U;
@@ -125,8 +253,33 @@ static hipError_t go_consume_sentinel_shape(Ptrs<u32x4*> p, u32x4* out, uint64_t
 // The consumer keeps one 64-pack group per lane at every size: a second group
 // per lane would hold 2*N 16-byte packs in registers for the re-arm pass.
 template <int N>
+static hipError_t go_consume_sentinel_two_pass(Ptrs<u32x4*> p, u32x4* out, uint64_t* bitmap,
+                                               size_t npacks, hipStream_t stream) {
+    uint32_t ntiles = (uint32_t)((npacks + kSFTilePacks - 1) / kSFTilePacks);
+    const uint32_t slots = 2 * device_cus();
+    const uint32_t rounds = (ntiles + slots - 1) / slots;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    void* args[] = {&p, &out, &bitmap, &npacks, &ntiles};
+    hipError_t e = hipLaunchKernel((const void*)&k_sentinel_fold_persistent<N, kSFBatch>, dim3(grid),
+                                   dim3(4 * kWave), args, 0, stream);
+    if (e != hipSuccess) return e;
+    constexpr size_t kBlockPacks = 4 * kWave * kRearmGroups;
+    dim3 rgrid((unsigned)((npacks + kBlockPacks - 1) / kBlockPacks), (unsigned)N);
+    const uint64_t* b = bitmap;
+    void* rargs[] = {&p, &b, &npacks};
+    return hipLaunchKernel((const void*)&k_sentinel_rearm<kPolicyNonTemporal>, rgrid, dim3(4 * kWave), rargs, 0, stream);
+}
+
+template <int N>
 static hipError_t go_consume_sentinel(Ptrs<u32x4*> p, u32x4* out, uint64_t* bitmap, size_t npacks,
                                       hipStream_t stream) {
+    // Slots read plus results and re-arms written.  From 768 MiB, three times
+    // the last-level cache, the two passes are faster (8 ranks: 197 vs 226 us
+    // at 64 MiB per rank, 147 vs 165 at 48, 294 vs 333 at 96); below it the
+    // single kernel keeps more in the caches (101 vs 104 us at 32 MiB) and a
+    // second launch costs more than it saves at decode sizes.
+    if (npacks * 16 * (2 * (size_t)N + 1) >= ((size_t)768 << 20))
+        return go_consume_sentinel_two_pass<N>(p, out, bitmap, npacks, stream);
     return go_consume_sentinel_shape<N, 4, 1>(p, out, bitmap, npacks, stream);
 }
 

@@ -668,6 +668,31 @@ def test_consume_sentinel_shapes(B, D, orc, n, k):
     assert all(np.array_equal(g, w) for g, w in zip(got_slots, want_slots))
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_consume_sentinel_bandwidth_regime(B, D, orc, n):
+    # From 768 MiB of slots read plus results and re-arms written the call
+    # runs as a persistent fold and a separate re-arm pass.  Three 512-element
+    # units past that size leave ragged last blocks; ranks 0, 3 and 6 have
+    # about 2% of their packs missing and 1% torn (upper half unwritten).
+    k = (-(-(768 << 20) // (2 * (2 * n + 1))) // 512 + 3) * 512
+    say("consume_sentinel bandwidth regime", n, k)
+    pick = np.random.default_rng(900 + n)
+    slots = []
+    for r in range(n):
+        slot = orc.publish_sentinel(synth.uniform_bf16(900 + n, 0, r, k))
+        if r % 3 == 0:
+            roll = pick.random(k // 8)
+            slot = synth.unarrive(slot, roll < 0.02, (roll >= 0.02) & (roll < 0.03))
+        slots.append(slot)
+    want_out, want_bm, want_slots = orc.consume_sentinel(slots, k)
+    got_out, got_bm, got_slots = gpu_consume_sentinel(B, D, [D.up(s) for s in slots], k)
+    assert np.array_equal(got_bm, want_bm)
+    assert np.array_equal(got_out, want_out)
+    assert all(np.array_equal(g, w) for g, w in zip(got_slots, want_slots))
+    del slots, got_slots, want_slots
+    torch.cuda.empty_cache()
+
+
 def test_consume_sentinel_late_arrival(B, D, orc):
     case = synth.SentinelCase("late", 80, 8, 8192)
     xs, ms = case.payloads(), case.masks()
