@@ -35,7 +35,9 @@ constexpr int kStageLoads = (kGroupPieces + kGBlock - 1) / kGBlock;  // 3 per la
 // load, wait, write had serialised them).  Output stores carry the
 // non-temporal hint: the gathered output is written once here and read by a
 // later operation, and keeping it from displacing the shards in the caches
-// measured 22% faster on the 8 x 2 MiB workload.
+// measured 22% faster on the 8 x 2 MiB workload.  kLoadPolicy is the staging
+// loads' cache policy: default, or non-temporal for calls far larger than
+// the last-level cache (chosen at launch).
 template <int kLoadPolicy>
 __global__ __launch_bounds__(kGBlock) void k_allgather(Ptrs<const u32x4*> shards, u32x4* out,
                                                         uint64_t* bitmap, uint64_t seq,

@@ -15,6 +15,8 @@
 // bf16 = 16 bytes, published with one 16-byte store.  Because every NaN
 // result of the fold is narrowed to the canonical 0x7FC0, no fold result can
 // equal the sentinel, so results can be republished without a further check.
+// The consumer is one kernel up to 768 MiB moved, and from there a fold pass
+// and a re-arm pass ordered by the stream.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 
