@@ -902,6 +902,96 @@ def test_graph_replays_match_oracle(B, D, orc):
             o.fill_(-1)                           # the next replay must rewrite them
 
 
+def test_graph_replays_bandwidth_regime(B, D, orc):
+    """Every large-size path captured once and replayed with new inputs from
+    torch's device RNG written eagerly between replays: 8 ranks x 48 MiB takes
+    the two-launch, flag-linked and fused twoshots with their large shapes,
+    the persistent LL and speculative consumers, the two-pass sentinel
+    consumer and the all-gather with non-temporal staging.  Outputs are
+    checked at sampled positions against the oracle run on the sampled
+    inputs; bitmaps, re-armed slots, attempts and the linked status word are
+    checked whole."""
+    n, k = 8, 24 << 20                        # 48 MiB per rank
+    nl = k // 2
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1950)
+    ins = [torch.empty(k, dtype=torch.int16, device=dev) for _ in range(n)]
+    outs = [torch.empty(k, dtype=torch.int16, device=dev) for _ in range(n)]
+    louts = [torch.empty(k, dtype=torch.int16, device=dev) for _ in range(n)]
+    ws = linked_workspace(B, n, k)
+    lines = [torch.empty(nl, dtype=torch.int64, device=dev) for _ in range(n)]
+    ll_out = torch.empty(k, dtype=torch.int16, device=dev)
+    ll_bm = torch.empty(nl // 64, dtype=torch.int64, device=dev)
+    slots = [torch.full((k,), -1, dtype=torch.int16, device=dev) for _ in range(n)]
+    s_out = torch.empty(k, dtype=torch.int16, device=dev)
+    s_bm = torch.empty(k // 512, dtype=torch.int64, device=dev)
+    flags = [torch.full((k // 8192,), 3, dtype=torch.int32, device=dev) for _ in range(n)]
+    v_out = torch.empty(k, dtype=torch.int16, device=dev)
+    v_att = torch.empty(k // 8192, dtype=torch.int32, device=dev)
+    sb = 2 * k                                 # all-gather shard bytes
+    blocks = sb // 128
+    recs = [torch.empty(blocks * 17, dtype=torch.int64, device=dev) for _ in range(n)]
+    a_out = torch.empty(n * k, dtype=torch.int16, device=dev)
+    a_bm = torch.empty(n * blocks // 64, dtype=torch.int64, device=dev)
+
+    def rewrite():
+        for t in ins:
+            t.copy_(torch.randint(-32768, 32768, (k,), dtype=torch.int32, device=dev, generator=gen))
+        for rc in recs:
+            rc.copy_(torch.randint(-(1 << 62), 1 << 62, (blocks * 17,), dtype=torch.int64, device=dev,
+                                   generator=gen))
+            rc.view(blocks, 17)[:, 0] = 11
+
+    rewrite()
+    B.pc_twoshot_linked(ins, louts, k, ws)    # one eager call before capture
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            B.pc_twoshot(ins, outs, k)
+            B.pc_twoshot_fused(ins, outs, k)
+            B.pc_twoshot_linked(ins, louts, k, ws)
+            for r in range(n):
+                B.pc_pack_ll(ins[r], lines[r], k, 9)
+            B.pc_consume_ll(lines, ll_out, k, 9, ll_bm)
+            for r in range(n):
+                B.pc_publish_sentinel(ins[r], slots[r], k)
+            B.pc_consume_sentinel(slots, s_out, k, s_bm)
+            B.pc_reduce_validated(ins, flags, v_out, k, 8192, 3, 2, v_att)
+            B.pc_allgather_copy(recs, a_out, sb, 11, a_bm)
+    torch.cuda.synchronize()
+    idx_np = np.concatenate([np.arange(0, 4096), np.arange(k - 4096, k),
+                             np.random.default_rng(1950).integers(0, k, 1 << 16)])
+    idx = torch.from_numpy(idx_np).to(dev)
+    blk = torch.from_numpy(np.random.default_rng(1951).integers(0, blocks, 4096)).to(dev)
+    for rep in range(3):
+        rewrite()
+        ll_bm.zero_()
+        s_bm.zero_()
+        a_bm.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        say("bandwidth-regime graph replay", rep)
+        xs = [D.down(t[idx], np.uint16) for t in ins]
+        want = orc.reduce(xs)
+        for t in outs + louts + [ll_out, v_out]:
+            assert np.array_equal(D.down(t[idx], np.uint16), want), rep
+        assert np.array_equal(D.down(s_out[idx], np.uint16),
+                              orc.reduce([orc.publish_sentinel(x) for x in xs])), rep
+        assert bool((ll_bm == -1).all()) and bool((s_bm == -1).all()) and bool((a_bm == -1).all())
+        assert all(bool((t == -1).all()) for t in slots)
+        assert bool((v_att == 1).all())
+        assert int(ws[B.PC_LINKED_STATUS_WORD]) == 0
+        for r in range(n):
+            got = a_out.view(n, blocks, 64)[r][blk]
+            src = recs[r].view(blocks, 17)[blk][:, 1:].contiguous().view(torch.int16)
+            assert torch.equal(got, src.view(-1, 64)), (rep, r)
+    del ins, outs, louts, lines, slots, recs, a_out
+    torch.cuda.empty_cache()
+
+
 def test_graph_replays_of_the_other_calls(B, D, orc):
     """Copy, two-launch twoshot, all-gather, sentinel publish + consume and the
     speculative reduce captured once and replayed with new inputs written
