@@ -58,6 +58,34 @@ __global__ __launch_bounds__(W * kWave) void k_publish_sentinel(const u32x4* src
     }
 }
 
+// Bandwidth regime: a persistent grid of two workgroups per CU, one 16 KiB
+// tile per step (load, barrier, store), as the Atom copy's persistent kernel.
+// Publishing in place is safe: a tile is read and then written by the same
+// workgroup, and tiles do not overlap.
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void k_publish_sentinel_persistent(const u32x4* src, u32x4* dst, size_t nchunks, uint32_t ntiles) {
+    constexpr int U = 4;
+    constexpr uint32_t kTile = 4 * kWave * U;
+    const uint32_t t = threadIdx.x;
+    for (uint32_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
+        const size_t first = (size_t)g * kTile;
+        const size_t left = nchunks - first;
+        const uint32_t bytes = (uint32_t)(left < kTile ? left : kTile) * 16u;
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src + first, bytes);
+        const __amdgpu_buffer_rsrc_t rd = tile_rsrc(dst + first, bytes);
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = load16_rsrc<kPolicyNonTemporal>(rs, (u * 4 * kWave + t) * 16u);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[u][e] = sanitize(v[u][e]);
+            store16_rsrc<kPolicyDeviceScope>(rd, (u * 4 * kWave + t) * 16u, v[u]);
+        }
+    }
+}
+
 // ---- consume: every wave owns U groups of 64 consecutive packs --------------------
 // Lane l of group u takes pack base + 64u + l from every rank's slot; the
 // wave's ballot over "no rank holds the sentinel anywhere in the pack" is the
@@ -238,6 +266,20 @@ static hipError_t go_publish(const u32x4* s, u32x4* d, size_t nchunks, hipStream
 hipError_t launch_publish_sentinel(const void* src, void* dst, size_t nchunks, hipStream_t stream) {
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
+    // Bytes read plus written.  From 512 MiB, twice the last-level cache, the
+    // persistent kernel is ahead (256 MiB per call: 76 vs 92 us); below it the
+    // one-tile-per-workgroup kernel keeps its cache help (38.2 vs 39.3 us at
+    // 128 MiB).
+    if (nchunks * 32 >= ((size_t)512 << 20)) {
+        constexpr uint32_t kTile = 4 * kWave * 4;
+        uint32_t ntiles = (uint32_t)((nchunks + kTile - 1) / kTile);
+        const uint32_t slots = 2 * device_cus();
+        const uint32_t rounds = (ntiles + slots - 1) / slots;
+        const uint32_t grid = (ntiles + rounds - 1) / rounds;
+        void* args[] = {&s, &d, &nchunks, &ntiles};
+        return hipLaunchKernel((const void*)&k_publish_sentinel_persistent, dim3(grid), dim3(4 * kWave), args, 0,
+                               stream);
+    }
     if (nchunks * 16 < kSentinelSmallBytes) return go_publish<4, 1>(s, d, nchunks, stream);
     return go_publish<4, 2>(s, d, nchunks, stream);
 }

@@ -635,6 +635,26 @@ def test_publish_sentinel_bits(B, D, orc):
     assert np.array_equal(D.down(gpu_publish(B, D, x), np.uint16), orc.publish_sentinel(x))
 
 
+@pytest.mark.parametrize("chunks,in_place", [((1 << 24) + 5, False), ((1 << 24) + 1027, True),
+                                             ((1 << 24) - 1024, False)])
+def test_publish_sentinel_bandwidth_regime(B, D, orc, chunks, in_place):
+    # From 512 MiB read plus written the publisher is a persistent kernel; the
+    # first two sizes are just past that (ragged last tile, one in place), the
+    # third just below.  Uniformly random bit patterns include the sentinel.
+    k = 8 * chunks
+    say("publish bandwidth regime", k, in_place)
+    x = np.random.default_rng(chunks).integers(0, 1 << 16, k, dtype=np.uint32).astype(np.uint16)
+    want = orc.publish_sentinel(x)
+    if in_place:
+        t = D.up(x)
+        B.pc_publish_sentinel(t, t, k)
+        got = D.down(t, np.uint16)
+    else:
+        got = D.down(gpu_publish(B, D, x), np.uint16)
+    assert np.array_equal(got, want)
+    torch.cuda.empty_cache()
+
+
 def test_consume_sentinel_128k_workload(B, D, orc):
     case = synth.C2S_SENTINEL_128K
     say(case.name)
