@@ -45,6 +45,34 @@ __global__ __launch_bounds__(W * kWave) void k_pack_ll(const u32x4* src, u32x4* 
     }
 }
 
+// From 4 MiB per rank: a lane takes 8 input bytes (4 bf16) and writes the two
+// lines they make as one 16-byte store, so a wave reads 512 B and writes
+// 1 KiB, both contiguous.  (The kernel above writes two 16-byte chunks per
+// lane, so each of its store instructions covers every other chunk of the
+// output.)  At one rank: 8.6 vs 9.8 us at 16 MiB, 29.6 vs 30.7 at 64 MiB and
+// 137 vs 152 at 256 MiB; at 128 KiB the kernel above is 0.03 us faster.
+template <int W, int U>
+__global__ __launch_bounds__(W * kWave) void k_pack_ll_half(const u32x2* src, u32x4* dst, uint32_t seq,
+                                                             size_t nhalf) {
+    constexpr int kBlk = W * kWave;
+    const size_t tile0 = (size_t)blockIdx.x * (kBlk * U);
+    u32x2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t c = tile0 + u * kBlk + threadIdx.x;
+        if (c < nhalf) v[u] = src[c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t c = tile0 + u * kBlk + threadIdx.x;
+        if (c < nhalf) {
+            u32x4 a;
+            a[0] = v[u][0]; a[1] = seq; a[2] = v[u][1]; a[3] = seq;
+            dst[c] = a;
+        }
+    }
+}
+
 // ---- consume: every wave owns U groups of 64 consecutive lines ------------------
 // Lane l of group u takes line base + 64u + l from every rank.  The wave's
 // ballot over "all ranks carry seq" is exactly the 64-bit bitmap word of the
@@ -214,7 +242,12 @@ hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t s
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
     if (nchunks * 16 < kSmallBytes) return go_pack<4, 1>(s, d, seq, nchunks, stream);
-    return go_pack<4, 2>(s, d, seq, nchunks, stream);
+    const u32x2* h = reinterpret_cast<const u32x2*>(src);
+    size_t nhalf = nchunks * 2;
+    constexpr size_t kTile = 4 * kWave * 2;
+    dim3 grid((unsigned)((nhalf + kTile - 1) / kTile));
+    void* args[] = {&h, &d, &seq, &nhalf};
+    return hipLaunchKernel((const void*)&k_pack_ll_half<4, 2>, grid, dim3(4 * kWave), args, 0, stream);
 }
 
 template <int N, int W, int U>
