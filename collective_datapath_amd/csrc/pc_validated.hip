@@ -112,8 +112,9 @@ void k_reduce_validated_persistent(Ptrs<const u32x4*> src, Ptrs<const uint32_t*>
                                    uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
                                    uint32_t ntiles) {
     // Tiles per batch, from a sweep at 8 ranks x 64 MiB: 16 for one or two
-    // chunks per lane, 8 for four (32 chunks, as in the persistent reduce).
-    constexpr int kBatch = U == 4 ? 8 : 16;
+    // chunks per lane, 8 for four (32 chunks, as in the persistent reduce),
+    // and 2 for three (the only batch that compiled without spilling).
+    constexpr int kBatch = U == 4 ? 8 : (U == 3 ? 2 : 16);
     constexpr uint32_t kTile = kBlock * U;
     static_assert(kBatch <= 32, "one bit per tile of a batch");
     __shared__ uint32_t passed_lds, again_lds;
@@ -248,9 +249,8 @@ static hipError_t go_validated_persistent_u(int u, Ptrs<const u32x4*> s, Ptrs<co
     switch (u) {
         case 1: return go_validated_persistent<N, 1>(s, f, out, flag, max_attempts, attempts, tiles, stream);
         case 2: return go_validated_persistent<N, 2>(s, f, out, flag, max_attempts, attempts, tiles, stream);
+        case 3: return go_validated_persistent<N, 3>(s, f, out, flag, max_attempts, attempts, tiles, stream);
         case 4: return go_validated_persistent<N, 4>(s, f, out, flag, max_attempts, attempts, tiles, stream);
-        // Three chunks per lane spilled registers at every batch size tried
-        // (4x slower); that spacing keeps the one-tile-per-workgroup kernel.
         default: return go_validated_u<N>(u, s, f, out, flag, max_attempts, attempts, tiles, stream);
     }
 }

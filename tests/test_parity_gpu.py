@@ -838,8 +838,8 @@ def test_reduce_validated_in_place(B, D, orc):
 
 # Working sets of 64 MiB and more run on the persistent kernel (two workgroups
 # per CU taking batches of 16 or 8 tiles).  These tile counts leave the last
-# batch of most workgroups partly empty; 6144 elements per flag stays on the
-# one-tile-per-workgroup kernel at every size.  The flag's multiple wraps
+# batch of most workgroups partly empty (6144 elements per flag takes batches
+# of 2 tiles, the other spacings 16 or 8).  The flag's multiple wraps
 # mod 2^32, and a tenth of the tiles carry a stale flag on some rank.
 @pytest.mark.parametrize("n,t,tiles,in_place", [(8, 8192, 515, False), (8, 2048, 2053, False),
                                                 (8, 4096, 1030, False), (2, 4096, 2737, False),
