@@ -12,7 +12,7 @@
 // monotonically (SiFAR, Section 8.1).
 //
 // Tile b (elems_per_flag elements) is validated by flag word b of every
-// rank.  Below a 64 MiB working set each tile has a workgroup of
+// rank.  Below a 320 MiB working set each tile has a workgroup of
 // elems_per_flag / 8 lanes; from there a persistent grid takes the tiles in
 // batches.  The retry loop is bounded by max_attempts so every kernel ends;
 // attempts[b] receives the attempt that validated (1-based) or 0.
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kLanes) void k_reduce_validated(Ptrs<const u32x4*> 
     if (t == 0) attempts[b] = accepted;
 }
 
-// Bandwidth regime (working sets of 64 MiB and more): a persistent grid of
+// Bandwidth regime (working sets of 320 MiB and more): a persistent grid of
 // two 256-lane workgroups per CU, the structure of the persistent reduce.
 // Workgroup w takes tiles w, w + grid, ... in batches of kBatch; lane t holds
 // chunks t, t + 256, ... (U = elems_per_flag / 2048 of them) of each tile.
@@ -268,7 +268,12 @@ hipError_t launch_reduce_validated(const void* const* src, const void* const* fl
     uint32_t* at = static_cast<uint32_t*>(attempts);
     const int u = (int)(elems_per_flag / 2048);
     const size_t tiles = k / elems_per_flag;
-    if ((size_t)(n + 1) * k * 2 >= ((size_t)64 << 20)) {
+    // Inputs read plus the result written.  From 320 MiB the persistent kernel
+    // is ahead (8 ranks, one flag per 8192 elements: 60 vs 72 us at 40 MiB per
+    // rank = 360 MiB, 92 vs 116 us at 64 MiB); below it the one-tile kernel is
+    // (50 vs 53 us at 32 MiB = 288 MiB, 14 vs 30 us at 8 MiB, where most
+    // batches are part-empty).
+    if ((size_t)(n + 1) * k * 2 >= ((size_t)320 << 20)) {
         switch (n) {
             case 1: return go_validated_persistent_u<1>(u, s, f, o, flag, max_attempts, at, tiles, stream);
             case 2: return go_validated_persistent_u<2>(u, s, f, o, flag, max_attempts, at, tiles, stream);

@@ -836,20 +836,20 @@ def test_reduce_validated_in_place(B, D, orc):
     assert np.array_equal(D.down(ins[1], np.uint16), orc.reduce(xs))
 
 
-# Working sets of 64 MiB and more run on the persistent kernel (two workgroups
-# per CU taking batches of 16 or 8 tiles).  These tile counts leave the last
-# batch of most workgroups partly empty (6144 elements per flag takes batches
-# of 2 tiles, the other spacings 16 or 8).  The flag's multiple wraps
-# mod 2^32, and a tenth of the tiles carry a stale flag on some rank.
-@pytest.mark.parametrize("n,t,tiles,in_place", [(8, 8192, 515, False), (8, 2048, 2053, False),
-                                                (8, 4096, 1030, False), (2, 4096, 2737, False),
-                                                (1, 8192, 2051, False), (5, 6144, 913, False),
-                                                (3, 2048, 4099, False), (6, 4096, 1173, False),
-                                                (7, 8192, 517, False), (4, 8192, 821, True)])
+# Working sets of 320 MiB and more run on the persistent kernel (two
+# workgroups per CU taking batches of 16, 8 or, at 6144 elements per flag, 2
+# tiles).  Three tiles past that size leave the last batch of most workgroups
+# partly empty.  The flag's multiple wraps mod 2^32, and a tenth of the tiles
+# carry a stale flag on some rank.
+@pytest.mark.parametrize("n,t,tiles,in_place", [(8, 8192, 2279, False), (8, 2048, 9106, False),
+                                                (8, 4096, 4555, False), (2, 4096, 13657, False),
+                                                (1, 8192, 10243, False), (5, 6144, 4555, False),
+                                                (3, 2048, 20483, False), (6, 4096, 5855, False),
+                                                (7, 8192, 2563, False), (4, 8192, 4099, True)])
 def test_reduce_validated_bandwidth_regime(B, D, orc, n, t, tiles, in_place):
     k = t * tiles
     say("validated bandwidth regime", n, t, tiles, in_place)
-    assert (n + 1) * 2 * k >= 64 << 20
+    assert (n + 1) * 2 * k >= 320 << 20
     case = synth.ValidatedCase("vb", 95 + n, n, k, t, flag=0x9E3779B9, stale_frac=0.1)
     xs, fl = case.payloads(), case.flags()
     # A tile that never validates leaves out untouched: prefilled with
