@@ -36,8 +36,7 @@ PC_SENTINEL = 0xFFFF
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-        "or `python collective_datapath_amd/build.py` first")
+        f"{LIB_PATH} is not built; run `python collective_datapath_amd/build.py` first")
 
 # torch owns device memory and streams, so the library must run on torch's HIP
 # runtime.  Loading torch first makes the dynamic linker resolve the library's

@@ -14,7 +14,7 @@ EXE = os.path.join(HERE, "c_abi", "pc_abi_check")
 
 def exe():
     if not os.path.exists(EXE):
-        pytest.skip("tests/c_abi/pc_abi_check is not built (run __graft_entry__.build())")
+        pytest.skip("tests/c_abi/pc_abi_check is not built (run tests/c_abi/build.py)")
     return EXE
 
 
