@@ -1,9 +1,11 @@
-"""Byte offsets above 4 GiB for every entry point whose other tests stay
-below it (the reduce and the copy have their own).
+"""Byte offsets above 4 GiB, and the largest accepted size, for every entry
+point whose other tests stay below them (the reduce and the copy have their
+own).
 
-Each call runs once on buffers that reach past 2^32 bytes, with sizes ragged
-against every tile shape, so every kernel's address arithmetic is exercised
-where 32 bits no longer suffice.  Outputs are compared bit for bit with the
+Each call runs twice: on buffers that reach just past 2^32 bytes, with sizes
+ragged against every tile shape, and at the largest size it accepts
+(PC_MAX_ELEMS elements per rank, or twice that many bytes), so every
+kernel's address arithmetic is exercised where 32 bits no longer suffice.  Outputs are compared bit for bit with the
 oracle over sampled windows: the head, a window around each multiple of
 2^32 bytes of every buffer the call touches, and the tail.  Windows of the
 calls that write a bitmap start and end on whole bitmap words.
@@ -21,6 +23,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GiB = 1 << 30
 FAR = 1 << 32  # the byte offset every buffer under test reaches past
+MAX_ELEMS = 1 << 34  # PC_MAX_ELEMS of include/pc.h
+SIZES = ["past_4gib", "maximum"]
 
 
 def say(*a):
@@ -96,10 +100,12 @@ def plant(rng, span, frac):
 
 # ---- LL pack and consume ------------------------------------------------------------
 
-def test_pack_ll_past_4gib(B, D, orc):
-    k = FAR // 2 + 8 * 5  # src 4 GiB + 80 B, lines 8 GiB + 160 B
+@pytest.mark.parametrize("size", SIZES)
+def test_pack_ll_far(B, D, orc, size):
+    # past 4 GiB: src 4 GiB + 80 B, lines 8 GiB + 160 B
+    k = FAR // 2 + 8 * 5 if size == "past_4gib" else MAX_ELEMS
     need_memory(6 * k + GiB)
-    say("pack_ll past 4 GiB", k)
+    say("pack_ll", size, k)
     seq = 0x5EED0001
     src = finite_bf16(k, gen(41))
     lines = torch.empty(k // 2, dtype=torch.int64, device=DEV)
@@ -110,14 +116,15 @@ def test_pack_ll_past_4gib(B, D, orc):
         assert np.array_equal(D.down(lines[a:b], np.uint64), want), (a, b)
 
 
-def test_consume_ll_past_4gib(B, D, orc):
-    # 8 GiB + 1.5 KiB of lines per rank, 4 GiB + 768 B of output: the
-    # persistent consumer.  A tenth of each window's lines is stale on some
+@pytest.mark.parametrize("size", SIZES)
+def test_consume_ll_far(B, D, orc, size):
+    # Past 4 GiB: 8 GiB + 1.5 KiB of lines per rank, 4 GiB + 768 B of
+    # output (the persistent consumer).  A tenth of each window's lines is stale on some
     # rank, and one 64-line group is stale on rank 0 (a zero bitmap word).
-    n, k = 2, FAR // 2 + 128 * 3
+    n, k = 2, FAR // 2 + 128 * 3 if size == "past_4gib" else MAX_ELEMS
     nl = k // 2
     need_memory(n * 8 * nl + 2 * k + 6 * GiB)
-    say("consume_ll past 4 GiB", n, k)
+    say("consume_ll", size, n, k)
     seq = 0x0C0FFEE1
     g = gen(42)
     lines = []
@@ -144,9 +151,11 @@ def test_consume_ll_past_4gib(B, D, orc):
 
 # ---- twoshot, all three forms ------------------------------------------------------------
 
-def test_twoshot_forms_past_4gib(B, D, orc):
-    # 4 GiB + 224 B per rank: every byte offset past 4 GiB lies in slice 1.
-    n, k = 2, FAR // 2 + 16 * 7
+@pytest.mark.parametrize("size", SIZES)
+def test_twoshot_forms_far(B, D, orc, size):
+    # Past 4 GiB: 4 GiB + 224 B per rank, so every byte offset past 4 GiB
+    # lies in slice 1.
+    n, k = 2, FAR // 2 + 16 * 7 if size == "past_4gib" else MAX_ELEMS
     need_memory(4 * 2 * k + 2 * GiB)
     g = gen(43)
     ins = [finite_bf16(k, g) for _ in range(n)]
@@ -155,7 +164,7 @@ def test_twoshot_forms_past_4gib(B, D, orc):
     spans = windows(k, byte_marks(k, 2) + [k // n], 8192, align=8)
     wants = [orc.reduce([D.down(x[a:b], np.uint16) for x in ins]) for a, b in spans]
     for form in ("pc_twoshot", "pc_twoshot_fused", "pc_twoshot_linked"):
-        say(form, "past 4 GiB", n, k)
+        say(form, size, n, k)
         for o in outs:
             o.fill_(-1)
         if form == "pc_twoshot_linked":
@@ -171,15 +180,16 @@ def test_twoshot_forms_past_4gib(B, D, orc):
 
 # ---- all-gather of 136-byte records --------------------------------------------------------
 
-def test_allgather_past_4gib(B, D, orc):
-    # 4 GiB + 24 KiB of payload per shard: records reach 4.25 GiB and the
-    # output 8 GiB.  Headers are compared as u64: stale ones differ from seq
+@pytest.mark.parametrize("size", SIZES)
+def test_allgather_far(B, D, orc, size):
+    # Past 4 GiB: 4 GiB + 24 KiB of payload per shard, so records reach
+    # 4.25 GiB and the output 8 GiB.  Headers are compared as u64: stale ones differ from seq
     # only in the upper word.
     n = 2
-    shard_bytes = FAR + 8192 * 3
+    shard_bytes = FAR + 8192 * 3 if size == "past_4gib" else 2 * MAX_ELEMS
     bs = shard_bytes // 128
     need_memory(n * 136 * bs + n * shard_bytes + 2 * GiB)
-    say("allgather past 4 GiB", n, shard_bytes)
+    say("allgather", size, n, shard_bytes)
     seq = (7 << 32) | 0x2468ACE1
     stale = seq ^ (1 << 40)
     g = gen(44)
@@ -210,10 +220,11 @@ def test_allgather_past_4gib(B, D, orc):
 
 # ---- sentinel publish and consume -------------------------------------------------------
 
-def test_publish_sentinel_past_4gib(B, D, orc):
-    k = FAR // 2 + 8 * 9  # 4 GiB + 144 B
+@pytest.mark.parametrize("size", SIZES)
+def test_publish_sentinel_far(B, D, orc, size):
+    k = FAR // 2 + 8 * 9 if size == "past_4gib" else MAX_ELEMS  # past 4 GiB: 4 GiB + 144 B
     need_memory(4 * k + GiB)
-    say("publish_sentinel past 4 GiB", k)
+    say("publish_sentinel", size, k)
     src = finite_bf16(k, gen(45))
     spans = windows(k, byte_marks(k, 2), 8192, align=8)
     rng = np.random.default_rng(45)
@@ -226,13 +237,14 @@ def test_publish_sentinel_past_4gib(B, D, orc):
         assert np.array_equal(D.down(slot[a:b], np.uint16), want), (a, b)
 
 
-def test_consume_sentinel_past_4gib(B, D, orc):
-    # 4 GiB + 3 KiB per slot: the two-pass consumer.  A few elements of each
+@pytest.mark.parametrize("size", SIZES)
+def test_consume_sentinel_far(B, D, orc, size):
+    # Past 4 GiB: 4 GiB + 3 KiB per slot (the two-pass consumer).  A few elements of each
     # window hold the sentinel on every rank, and one 64-pack group is still
     # armed on rank 1.
-    n, k = 2, FAR // 2 + 512 * 3
+    n, k = 2, FAR // 2 + 512 * 3 if size == "past_4gib" else MAX_ELEMS
     need_memory(3 * 2 * k + 2 * GiB)
-    say("consume_sentinel past 4 GiB", n, k)
+    say("consume_sentinel", size, n, k)
     g = gen(46)
     slots = [finite_bf16(k, g) for _ in range(n)]
     spans = windows(k, byte_marks(k, 2), 16384, align=512)
@@ -256,15 +268,16 @@ def test_consume_sentinel_past_4gib(B, D, orc):
 
 # ---- speculative reduce with a folded flag ---------------------------------------------
 
-def test_reduce_validated_past_4gib(B, D, orc):
-    # 4 GiB + 48 KiB per rank at 8192 elements per flag (the persistent
+@pytest.mark.parametrize("size", SIZES)
+def test_reduce_validated_far(B, D, orc, size):
+    # Past 4 GiB: 4 GiB + 48 KiB per rank, at 8192 elements per flag (the persistent
     # kernel with four chunks per lane); a quarter of each window's tiles
     # carries a stale flag on rank 1 and is left untouched.
     n, t = 2, 8192
-    tiles = FAR // (2 * t) + 3
+    tiles = FAR // (2 * t) + 3 if size == "past_4gib" else MAX_ELEMS // t
     k = t * tiles
     need_memory(3 * 2 * k + GiB)
-    say("reduce_validated past 4 GiB", n, k, t)
+    say("reduce_validated", size, n, k, t)
     flag = 0x9E3779B9
     as_i32 = lambda v: v - (1 << 32) if v >= 1 << 31 else v  # noqa: E731
     g = gen(47)
