@@ -18,7 +18,9 @@
 // product (Purlin, Section 3.3, Equation (3)).  Cache-resident payloads use
 // one workgroup per tile (k_reduce); payloads far beyond the last-level cache
 // use a persistent grid (k_reduce_persistent).  Three output modes cover the
-// oneshot reduce, twoshot phase 1 and the single-launch twoshot.
+// oneshot reduce, twoshot phase 1 and the single-launch twoshot; at the
+// largest sizes the single-launch twoshot folds first and hands its tiles
+// out afterwards, in the same launch (k_twoshot_persistent).
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 
@@ -167,6 +169,51 @@ void k_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nsli
             reduce_batch<N, kOut, kBatch, true>(src, dst, nslice, tiles_per_slice, ntiles, g0, stride);
         else
             reduce_batch<N, kOut, kBatch, false>(src, dst, nslice, tiles_per_slice, ntiles, g0, stride);
+    }
+}
+
+// ---- single-launch twoshot, bandwidth regime: fold, then hand out ---------------
+// Each workgroup first folds its tiles as twoshot phase 1 does, into the
+// owner's output only (N input streams, one output stream), and only then
+// reads those tiles back and writes them to the N-1 other outputs (one input
+// stream, N-1 output streams, non-temporal as in the copy-out at these
+// sizes): the two-launch form's traffic in one launch.  No workgroup reads
+// what another one wrote.  Every byte position belongs to one tile, and
+// every access to it, in any buffer, is made by the workgroup that owns that
+// tile; a lane reads back exactly the chunks it stored, after all of the
+// workgroup's stores have completed, with device-scope loads that the L2
+// serves (the stores wrote through to it).  So no flag, no fence between
+// workgroups and no workspace is needed, and exact aliasing of inputs and
+// outputs stays safe.
+template <int N>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
+void k_twoshot_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                          uint32_t tiles_per_slice, uint32_t ntiles) {
+    constexpr int kBatch = batch_tiles<N, Out::kOwner>();
+    constexpr int U = 4;
+    constexpr uint32_t kTile = kBlock * U;
+    const uint32_t stride = gridDim.x;
+    for (uint32_t g0 = blockIdx.x; g0 < ntiles; g0 += stride * kBatch) {
+        if (g0 + (kBatch - 1) * stride < ntiles)
+            reduce_batch<N, Out::kOwner, kBatch, true>(src, dst, nslice, tiles_per_slice, ntiles, g0, stride);
+        else
+            reduce_batch<N, Out::kOwner, kBatch, false>(src, dst, nslice, tiles_per_slice, ntiles, g0, stride);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    __syncthreads();
+    const uint32_t t = threadIdx.x;
+    for (uint32_t g = blockIdx.x; g < ntiles; g += stride) {
+        const TileAt at = tile_at<Out::kOwner>(g, nslice, tiles_per_slice, kTile);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(dst.p[at.s] + at.first, at.bytes);
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = load16_rsrc<kPolicyDeviceScope>(rs, (u * kBlock + t) * 16u);
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            const __amdgpu_buffer_rsrc_t rd = tile_rsrc(dst.p[r] + at.first, (uint32_t)r == at.s ? 0u : at.bytes);
+#pragma unroll
+            for (int u = 0; u < U; ++u) store16_rsrc<kPolicyNonTemporal>(rd, (u * kBlock + t) * 16u, v[u]);
+        }
     }
 }
 
@@ -342,15 +389,52 @@ hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size
     }
 }
 
+// The single-launch twoshot folds first and hands out after (the kernel
+// above) from a working set, inputs plus outputs, of 768 MiB (three times
+// the last-level cache) with five or more ranks.  A/B on one box, µs, the
+// kernel above against the single fan-out pass: 8 ranks 229 vs 246-249 at
+// 64 MiB per rank and 168-170 vs 176 at 48 (even at 40, 101 vs 82 at 32);
+// 7 ranks 215 vs 244 at 72 MiB and 162-167 vs 176-178 at 56 (103-106 vs
+// 100 at 40); 6 ranks 163 vs 172-175 at 64 MiB and 317-321 vs 353-355 at
+// 128; 5 ranks 171-173 vs 191-195 at 96 MiB.  The read-back adds 1/n of
+// the traffic, so with fewer ranks the fan-out pass stays ahead (4 ranks:
+// even at 128 MiB per rank, 104 vs 84-85 at 64).
+constexpr size_t kSplitWorkingSet = (size_t)768 << 20;
+constexpr int kSplitMinRanks = 5;
+
+template <int N>
+static hipError_t go_twoshot_split(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                                   hipStream_t stream) {
+    constexpr uint32_t kTile = kBlock * 4;
+    uint32_t tiles_per_slice = (nslice + kTile - 1) / kTile;
+    uint32_t ntiles = tiles_per_slice * N;
+    const uint32_t slots = 2 * device_cus();
+    const uint32_t rounds = (ntiles + slots - 1) / slots;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    void* args[] = {&src, &dst, &nslice, &tiles_per_slice, &ntiles};
+    return hipLaunchKernel((const void*)&k_twoshot_persistent<N>, dim3(grid), dim3(kBlock), args, 0,
+                           stream);
+}
+
 hipError_t launch_twoshot_fused(const void* const* src, int n, void* const* outs,
                                 size_t nchunks_slice, hipStream_t stream) {
     Ptrs<const u32x4*> s;
     Ptrs<u32x4*> d = {};
     fill_src(s, src, n);
     for (int r = 0; r < n; ++r) d.p[r] = static_cast<u32x4*>(outs[r]);
-    // The fused call reads each input once and writes every output once.
+    // Working set: every input read once and every output written once.
     const size_t per_rank = nchunks_slice * (size_t)n;
     const Regime rg = pick_regime(per_rank, per_rank * 16 * 2 * (size_t)n);
+    if (n >= kSplitMinRanks && per_rank * 16 * 2 * (size_t)n >= kSplitWorkingSet) {
+        const uint32_t ns = (uint32_t)nchunks_slice;
+        switch (n) {
+            case 5: return go_twoshot_split<5>(s, d, ns, stream);
+            case 6: return go_twoshot_split<6>(s, d, ns, stream);
+            case 7: return go_twoshot_split<7>(s, d, ns, stream);
+            case 8: return go_twoshot_split<8>(s, d, ns, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     return dispatch_reduce<Out::kAll>(n, rg, s, d, (uint32_t)nchunks_slice, (uint32_t)n, stream);
 }
 

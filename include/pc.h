@@ -181,8 +181,11 @@ PC_API pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* cons
  * Same arguments, layouts, aliasing rules and errors as pc_twoshot, and the
  * same result bit for bit: slice s = [s*k/n, (s+1)*k/n) is folded in rank
  * order 0..n-1 exactly once, and the workgroup that folds a block writes it
- * to every outs[r] (owner first).  One kernel is enqueued; the owner's slice
- * is not read back.
+ * to every outs[r].  One kernel is enqueued.  Below a working set (inputs
+ * plus outputs) of 768 MiB, or with fewer than five ranks, each folded
+ * block goes to every output at once; from there the workgroup first writes
+ * all of its blocks to their owners' outputs and then reads them back from
+ * there to write the other outputs.
  */
 PC_API pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t* const* outs,
                                   size_t k, void* stream);

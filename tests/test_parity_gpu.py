@@ -488,6 +488,31 @@ def test_twoshot_copies_nontemporal(B, D, orc, n, per_rank_mib, extra):
     torch.cuda.empty_cache()
 
 
+# From a working set (inputs plus outputs) of 768 MiB with five or more
+# ranks, pc_twoshot_fused folds every tile into its owner's output first and
+# hands it out afterwards.  Slice sizes just below and past that switch for
+# 5..8 ranks, ragged against the tiles, once in place, and four ranks past
+# the size (which keep the single fan-out pass).
+@pytest.mark.parametrize("n,extra,in_place", [(8, -1, False), (8, 3, False), (8, 5, True), (7, 2, False),
+                                              (6, 1, False), (5, 7, False), (4, 9, False)])
+def test_twoshot_fused_fold_then_hand_out(B, D, orc, n, extra, in_place):
+    switch = 768 << 20
+    sc = switch // (32 * n * n) + extra                 # chunks per slice
+    k = 8 * n * sc
+    split = n >= 5 and 2 * n * (2 * k) >= switch
+    assert split == (n >= 5 and extra >= 0)
+    say("twoshot fused", n, k, "fold then hand out" if split else "single pass", "in place" if in_place else "")
+    xs = [synth.normal_bf16(1750 + n, 0, r, k) for r in range(n)]
+    want = orc.reduce(xs, threads=THREADS)
+    ins = [D.up(x) for x in xs]
+    outs = ins if in_place else [D.filled(k, 0xFFFF) for _ in range(n)]
+    B.pc_twoshot_fused(ins, outs, k)
+    for r, o in enumerate(outs):
+        assert np.array_equal(D.down(o, np.uint16), want), r
+    del ins, outs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode", TWOSHOT_MODES)
 def test_twoshot_in_place(B, D, orc, mode):
     n, k = 4, 8 * 4 * 999

@@ -178,6 +178,24 @@ def test_twoshot_forms_far(B, D, orc, size):
     assert int(ws[B.PC_LINKED_STATUS_WORD]) == 0
 
 
+def test_twoshot_fused_split_past_4gib(B, D, orc):
+    # Five ranks of 4 GiB + 280 B: the single-launch twoshot that folds its
+    # tiles into the owners' outputs first and hands them out afterwards.
+    n = 5
+    k = (FAR // 2 // (8 * n) + 7) * 8 * n
+    need_memory(2 * n * 2 * k + 2 * GiB)
+    say("pc_twoshot_fused split past 4 GiB", n, k)
+    g = gen(48)
+    ins = [finite_bf16(k, g) for _ in range(n)]
+    outs = [torch.full((k,), -1, dtype=torch.int16, device=DEV) for _ in range(n)]
+    spans = windows(k, byte_marks(k, 2) + [s * k // n for s in range(1, n)], 8192, align=8)
+    B.pc_twoshot_fused(ins, outs, k)
+    for a, b in spans:
+        want = orc.reduce([D.down(x[a:b], np.uint16) for x in ins])
+        for r, o in enumerate(outs):
+            assert np.array_equal(D.down(o[a:b], np.uint16), want), (r, a, b)
+
+
 # ---- all-gather of 136-byte records --------------------------------------------------------
 
 @pytest.mark.parametrize("size", SIZES)
