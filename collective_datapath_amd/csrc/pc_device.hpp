@@ -85,6 +85,38 @@ __device__ __forceinline__ void store16_tile(__amdgpu_buffer_rsrc_t rs, uint32_t
     store16_rsrc<kPolicyDeviceScope>(rs, byte_off, v);
 }
 
+// ---- tiles of a slice ---------------------------------------------------------
+// Slice s of `nslice` chunks starts at chunk s*nslice.  Its tiles of up to
+// `tile` chunks lie on a grid aligned to 8 chunks (128 bytes, one cache line)
+// of the buffer: tile j covers [base + j*tile, base + (j+1)*tile) clipped to
+// the slice, where base is the slice start rounded down to 8 chunks, so only
+// a slice's first tile can start off a line.  Tiles cut from an unaligned
+// slice start would put every wave access across cache lines.
+struct SliceTile {
+    size_t first;     // first chunk
+    uint32_t chunks;  // 0 .. tile
+};
+
+__host__ __device__ inline SliceTile slice_tile(uint32_t s, uint32_t j, size_t nslice, uint32_t tile) {
+    const size_t start = (size_t)s * nslice, end = start + nslice;
+    size_t lo = (start & ~(size_t)7) + (size_t)j * tile;
+    size_t hi = lo + tile;
+    lo = lo < start ? start : lo;
+    lo = lo > end ? end : lo;
+    hi = hi > end ? end : hi;
+    return {lo, (uint32_t)(hi - lo)};
+}
+
+// Tiles per slice: the most that any of `slices` slices needs.
+__host__ __device__ inline uint32_t slice_tiles(size_t nslice, uint32_t slices, uint32_t tile) {
+    size_t most = 0;
+    for (uint32_t s = 0; s < slices; ++s) {
+        const size_t n = (nslice + ((size_t)s * nslice) % 8 + tile - 1) / tile;
+        most = n > most ? n : most;
+    }
+    return (uint32_t)most;
+}
+
 // ---- bf16 <-> fp32 ----------------------------------------------------------
 // A 32-bit word holds two bf16: element 2i in bits 0..15, element 2i+1 in
 // bits 16..31.  Widening is exact: the bf16 bits become the upper fp32 half.

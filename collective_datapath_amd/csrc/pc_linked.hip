@@ -46,13 +46,6 @@ namespace pcdp {
 constexpr int kLinkBlock = 256;
 constexpr uint32_t kMaxPolls = 1u << 20;
 
-// Chunks of tile j of a slice of `slice_chunks` chunks, as a byte count.
-template <uint32_t kTile>
-__device__ __forceinline__ uint32_t tile_bytes(size_t slice_chunks, size_t j) {
-    const size_t left = slice_chunks - j * kTile;
-    return (uint32_t)(left < kTile ? left : kTile) * 16u;
-}
-
 template <int N, int U, bool kStream, bool kNtCopies>
 __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*> src,
                                                                 Ptrs<u32x4*> outs, uint32_t* ws,
@@ -78,9 +71,10 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
     // writes back or invalidates a whole L2 and they queue up per XCD.
     if (w < ntiles) {
         for (size_t t = w; t < ntiles; t += kLinkGroups) {
-            const size_t s = t / tiles_per_slice, j = t % tiles_per_slice;
-            const size_t c0 = s * slice_chunks + j * kTile;
-            const uint32_t bytes = tile_bytes<kTile>(slice_chunks, j);
+            const size_t s = t / tiles_per_slice;
+            const SliceTile st = slice_tile((uint32_t)s, (uint32_t)(t % tiles_per_slice), slice_chunks, kTile);
+            const size_t c0 = st.first;
+            const uint32_t bytes = st.chunks * 16u;
             u32x4 v[U][N];
 #pragma unroll
             for (int r = 0; r < N; ++r) {
@@ -125,9 +119,10 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
         __syncthreads();
         if (ready) {
             for (size_t t = first; t < ntiles; t += kLinkGroups) {
-                const size_t s = t / tiles_per_slice, j = t % tiles_per_slice;
-                const size_t c0 = s * slice_chunks + j * kTile;
-                const uint32_t bytes = tile_bytes<kTile>(slice_chunks, j);
+                const size_t s = t / tiles_per_slice;
+                const SliceTile st = slice_tile((uint32_t)s, (uint32_t)(t % tiles_per_slice), slice_chunks, kTile);
+                const size_t c0 = st.first;
+                const uint32_t bytes = st.chunks * 16u;
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(outs.p[s] + c0, bytes);
                 u32x4 v[U];
 #pragma unroll
@@ -158,8 +153,8 @@ static int linked_unroll(size_t nchunks_slice, int n) {
 }
 
 size_t linked_tiles(int n, size_t nchunks_slice) {
-    const size_t tile = (size_t)kLinkBlock * linked_unroll(nchunks_slice, n);
-    return (size_t)n * ((nchunks_slice + tile - 1) / tile);
+    const uint32_t tile = kLinkBlock * linked_unroll(nchunks_slice, n);
+    return (size_t)n * slice_tiles(nchunks_slice, (uint32_t)n, tile);
 }
 
 // Workgroups of `kernel` that fit on the device at once, cached per device
@@ -192,8 +187,7 @@ static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint32_t* ws, 
         if (dev >= 0 && dev < 64) known[dev].store(cap + 1, std::memory_order_relaxed);
     }
     if (cap < (int)kLinkGroups) return hipErrorCooperativeLaunchTooLarge;
-    const size_t tile = (size_t)kLinkBlock * U;
-    size_t tiles_per_slice = (slice_chunks + tile - 1) / tile;
+    size_t tiles_per_slice = slice_tiles(slice_chunks, N, kLinkBlock * U);
     void* args[] = {&s, &o, &ws, &slice_chunks, &tiles_per_slice};
     return hipLaunchKernel(kernel, dim3(kLinkGroups), dim3(kLinkBlock), args, 0, stream);
 }

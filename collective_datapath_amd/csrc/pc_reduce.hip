@@ -106,13 +106,19 @@ struct TileAt {
     uint32_t bytes;
 };
 
+// Several slices: tiles on the 128-byte-aligned grid of slice_tile().
 template <Out kOut>
 __device__ __forceinline__ TileAt tile_at(uint32_t g, uint32_t nslice, uint32_t tiles_per_slice,
                                           uint32_t tile_chunks) {
-    const uint32_t s = kOut == Out::kOne ? 0u : g / tiles_per_slice;
-    const uint32_t tile0 = (g - s * tiles_per_slice) * tile_chunks;
-    const uint32_t left = nslice - tile0;
-    return {s, (size_t)s * nslice + tile0, (left < tile_chunks ? left : tile_chunks) * 16u};
+    if constexpr (kOut == Out::kOne) {
+        const uint32_t tile0 = g * tile_chunks;
+        const uint32_t left = nslice - tile0;
+        return {0u, (size_t)tile0, (left < tile_chunks ? left : tile_chunks) * 16u};
+    } else {
+        const uint32_t s = g / tiles_per_slice;
+        const SliceTile st = slice_tile(s, g - s * tiles_per_slice, nslice, tile_chunks);
+        return {s, st.first, st.chunks * 16u};
+    }
 }
 
 // One batch: tiles g0, g0 + stride, ... (kBatch of them).  kAllValid: every
@@ -229,10 +235,9 @@ template <int N, int U, int kStorePolicy>
 __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t nslice) {
     constexpr uint32_t kTile = kBlock * U;
     const uint32_t s = blockIdx.y;
-    const uint32_t tile0 = blockIdx.x * kTile;
-    const size_t first = (size_t)s * nslice + tile0;
-    const uint32_t left = nslice - tile0;
-    const uint32_t bytes = (left < kTile ? left : kTile) * 16u;
+    const SliceTile st = slice_tile(s, blockIdx.x, nslice, kTile);
+    const size_t first = st.first;
+    const uint32_t bytes = st.chunks * 16u;
     const uint32_t t = threadIdx.x;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(outs.p[s] + first, bytes);
     u32x4 v[U];
@@ -292,7 +297,7 @@ template <int N, Out kOut>
 static hipError_t go_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                                        uint32_t slices, hipStream_t stream) {
     constexpr uint32_t kTile = kBlock * 4;
-    uint32_t tiles_per_slice = (nslice + kTile - 1) / kTile;
+    uint32_t tiles_per_slice = slice_tiles(nslice, slices, kTile);
     uint32_t ntiles = tiles_per_slice * slices;
     // Whole rounds of at most two workgroups per CU, then as few workgroups
     // as give that many rounds, so every workgroup does the same number of
@@ -342,11 +347,11 @@ static hipError_t go_copyout(Ptrs<u32x4*> outs, uint32_t nslice, uint32_t slices
                              bool nt, hipStream_t stream) {
     void* args[] = {&outs, &nslice};
     if (wide) {
-        dim3 grid((nslice + 2 * kBlock - 1) / (2 * kBlock), slices);
+        dim3 grid(slice_tiles(nslice, slices, 2 * kBlock), slices);
         const void* k = nt ? (const void*)&k_copyout<N, 2, kPolicyNonTemporal> : (const void*)&k_copyout<N, 2, 0>;
         return hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream);
     }
-    dim3 grid((nslice + kBlock - 1) / kBlock, slices);
+    dim3 grid(slice_tiles(nslice, slices, kBlock), slices);
     return hipLaunchKernel((const void*)&k_copyout<N, 1, 0>, grid, dim3(kBlock), args, 0, stream);
 }
 
@@ -406,7 +411,7 @@ template <int N>
 static hipError_t go_twoshot_split(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                                    hipStream_t stream) {
     constexpr uint32_t kTile = kBlock * 4;
-    uint32_t tiles_per_slice = (nslice + kTile - 1) / kTile;
+    uint32_t tiles_per_slice = slice_tiles(nslice, N, kTile);
     uint32_t ntiles = tiles_per_slice * N;
     const uint32_t slots = 2 * device_cus();
     const uint32_t rounds = (ntiles + slots - 1) / slots;
