@@ -51,9 +51,17 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
                                                      uint32_t nslice) {
     constexpr uint32_t kTile = kBlock * U;
     const uint32_t s = kOut == Out::kOne ? 0u : blockIdx.y;
-    const uint32_t tile0 = blockIdx.x * kTile;
-    const size_t first = (size_t)s * nslice + tile0;
-    const uint32_t left = nslice - tile0;
+    size_t first;
+    uint32_t left;
+    if constexpr (kOut == Out::kOne) {
+        const uint32_t tile0 = blockIdx.x * kTile;
+        first = tile0;
+        left = nslice - tile0;
+    } else {  // several slices: the 128-byte-aligned tiles of slice_tile()
+        const SliceTile st = slice_tile(s, blockIdx.x, nslice, kTile);
+        first = st.first;
+        left = st.chunks;
+    }
     const uint32_t t = threadIdx.x;
     const u32x4* in[N];
 #pragma unroll
@@ -287,7 +295,7 @@ template <int N, int U, bool kStream, Out kOut>
 static hipError_t go_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                             uint32_t slices, hipStream_t stream) {
     constexpr uint32_t kTile = kBlock * U;
-    dim3 grid((nslice + kTile - 1) / kTile, slices);
+    dim3 grid(slice_tiles(nslice, slices, kTile), slices);
     void* args[] = {&src, &dst, &nslice};
     return hipLaunchKernel((const void*)&k_reduce<N, U, kStream, kOut>, grid, dim3(kBlock), args,
                            0, stream);
