@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604522239,
+TRAFFIC = {"bytes": 604522218,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "0f43143a870cb5b9ed6fddb7dc4bed7f8de1119eba09e53718c3a8a7593d085f"}
+           "sha256": "763c6b40a069b203e138b9ca9eba801b31ad22524204d634a7c9727cba9c40f1"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
