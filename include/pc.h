@@ -187,7 +187,7 @@ PC_API pc_status pc_twoshot(const uint16_t* const* inputs, int n, uint16_t* cons
  * same result bit for bit: slice s = [s*k/n, (s+1)*k/n) is folded in rank
  * order 0..n-1 exactly once, and the workgroup that folds a block writes it
  * to every outs[r].  One kernel is enqueued.  Below a working set (inputs
- * plus outputs) of 768 MiB, or with fewer than five ranks, each folded
+ * plus outputs) of 640 MiB, or with fewer than five ranks, each folded
  * block goes to every output at once; from there the workgroup first writes
  * all of its blocks to their owners' outputs and then reads them back from
  * there to write the other outputs.

@@ -488,7 +488,7 @@ def test_twoshot_copies_nontemporal(B, D, orc, n, per_rank_mib, extra):
     torch.cuda.empty_cache()
 
 
-# From a working set (inputs plus outputs) of 768 MiB with five or more
+# From a working set (inputs plus outputs) of 640 MiB with five or more
 # ranks, pc_twoshot_fused folds every tile into its owner's output first and
 # hands it out afterwards.  Slice sizes just below and past that switch for
 # 5..8 ranks, ragged against the tiles, once in place, and four ranks past
@@ -496,7 +496,7 @@ def test_twoshot_copies_nontemporal(B, D, orc, n, per_rank_mib, extra):
 @pytest.mark.parametrize("n,extra,in_place", [(8, -1, False), (8, 3, False), (8, 5, True), (7, 2, False),
                                               (6, 1, False), (5, 7, False), (4, 9, False)])
 def test_twoshot_fused_fold_then_hand_out(B, D, orc, n, extra, in_place):
-    switch = 768 << 20
+    switch = 640 << 20
     sc = switch // (32 * n * n) + extra                 # chunks per slice
     k = 8 * n * sc
     split = n >= 5 and 2 * n * (2 * k) >= switch
