@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC = {"bytes": 604522096,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "41ff1620c776a0e5b803697b836cc0032754e71dffed34edf2f2c4c0b2b3fbf8"}
+           "sha256": "25af94106e87d985e6e331745034024280a2f1bd0c04f77b2ce97f972287c15a"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -654,8 +654,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the datapath on one GPU; multi-GPU runs "
-              "are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the datapath on one GPU; runs on several "
+              "GPUs are not supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

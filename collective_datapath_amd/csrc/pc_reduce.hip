@@ -404,11 +404,11 @@ hipError_t launch_twoshot(const void* const* src, int n, void* const* outs, size
 
 // The single-launch twoshot folds first and hands out after (the kernel
 // above) from a working set, inputs plus outputs, of 640 MiB (two and a half
-// times the last-level cache) with five or more ranks.  A/B on one box, µs,
+// times the last-level cache) with five or more ranks.  A/B on one MI355X, µs,
 // the kernel above against the single fan-out pass: 8 ranks 229 vs 246-249
 // at 64 MiB per rank, 168-170 vs 176 at 48; 7 ranks 215 vs 244 at 72 MiB;
 // 6 ranks 163 vs 172-175 at 64 MiB; 5 ranks 171-173 vs 191-195 at 96 MiB.
-// On another box: 8 ranks 112-113 vs 119 at 40 MiB and 128-129 vs 141-142
+// On another MI355X: 8 ranks 112-113 vs 119 at 40 MiB and 128-129 vs 141-142
 // at 44, but 103 vs 99-100 at 36 (a 576 MiB working set).  The read-back
 // adds 1/n of the traffic, so with fewer ranks the fan-out pass stays ahead
 // (4 ranks: even at 128 MiB per rank, 104 vs 84-85 at 64).

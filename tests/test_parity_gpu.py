@@ -685,7 +685,7 @@ def test_consume_sentinel_128k_workload(B, D, orc):
     say(case.name)
     xs, ms = case.payloads(), case.masks()
     # Each side publishes with its own code; unarrived/torn packs are then
-    # put back to the sentinel by the harness.
+    # put back to the sentinel by the test.
     dev = [synth.unarrive(D.down(gpu_publish(B, D, x), np.uint16), m, t) for x, (m, t) in zip(xs, ms)]
     host = [synth.unarrive(orc.publish_sentinel(x), m, t) for x, (m, t) in zip(xs, ms)]
     for a, b in zip(dev, host):
