@@ -143,7 +143,7 @@ def test_linked_workspace_bytes():
     assert linked_need(3, 3 * 8 * 257) == fixed + 4 * 6
     # Tiles lie on a grid of 8-chunk (128-byte) lines of the buffer.  Two
     # slices of 509 chunks: slice 1 starts 5 chunks into a line, so its tiles
-    # cover [504, 760), [760, 1016) and [1016, 1018) -> 3 tiles per slice.
+    # cover [509, 760), [760, 1016) and [1016, 1018) -> 3 tiles per slice.
     assert linked_need(2, 2 * 8 * 509) == fixed + 4 * 2 * 3
     # Slices that start on a line keep ceil(chunks / tile) tiles: 2 x 512.
     assert linked_need(2, 2 * 8 * 512) == fixed + 4 * 2 * 2
