@@ -1,7 +1,9 @@
 """Build the HIP datapath library (libpcdp.so) for gfx950, in-tree.
 
-One hipcc invocation compiles every source under csrc/ into
-collective_datapath_amd/libpcdp.so.  Flags that matter for bit-exactness:
+Every source under csrc/ is compiled by its own hipcc process (in parallel)
+into collective_datapath_amd/_build/, and the objects are linked into
+collective_datapath_amd/libpcdp.so.  The sources share no device symbols, so
+no relocatable device code is needed.  Flags that matter for bit-exactness:
 no fast-math, no fp contraction, and fp32 subnormals kept on the device.
 Packed-fp32 instruction selection is switched off (plain v_add_f32 per
 element).
@@ -12,15 +14,17 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpcdp.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden", "-ffp-contract=off", "-fno-fast-math",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,14 +36,28 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, f"-I{os.path.join(ROOT, 'include')}",
-           *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = f"-I{os.path.join(ROOT, 'include')}"
+    jobs = []
+    objs = []
+    for src in sources():
+        obj = os.path.join(OBJ_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
+        objs.append(obj)
+        jobs.append([hipcc, *HIPCC_FLAGS, *extra_flags, inc, "-c", src, "-o", obj])
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
+    tmp = out + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

@@ -16,13 +16,17 @@
 // issued before its first fold, which keeps N*U*16 bytes per lane in flight:
 // the gfx950 counterpart of sizing a copy pipeline to the bandwidth-delay
 // product (Purlin, Section 3.3, Equation (3)).  Cache-resident payloads use
-// one workgroup per tile (k_reduce); payloads far beyond the last-level cache
-// use a persistent grid (k_reduce_persistent).  Three output modes cover the
-// oneshot reduce, twoshot phase 1 and the single-launch twoshot; at the
-// largest sizes the single-launch twoshot folds first and hands its tiles
-// out afterwards, in the same launch (k_twoshot_persistent).
+// one workgroup per tile (k_reduce).  Payloads far beyond the last-level
+// cache use a persistent grid: with four or more ranks one workgroup per CU
+// whose loads go straight to LDS stages (k_reduce_staged, pc_staged.hpp),
+// otherwise two workgroups per CU whose loads land in registers
+// (k_reduce_persistent).  Three output modes cover the oneshot reduce,
+// twoshot phase 1 and the single-launch twoshot; at the largest sizes the
+// single-launch twoshot folds first and hands its tiles out afterwards, in
+// the same launch (k_twoshot_persistent).
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
+#include "pc_staged.hpp"
 
 namespace pcdp {
 
@@ -186,6 +190,45 @@ void k_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nsli
     }
 }
 
+// ---- bandwidth regime: LDS-staged persistent slice reduce --------------------------
+// The oneshot reduce and twoshot phase 1 beyond the caches: one workgroup per
+// CU, every wave streaming its rows through LDS stages (pc_staged.hpp), the
+// batch's results held in registers and stored after a barrier.  The grid
+// is sized to whole rounds of one workgroup per CU, with equal tiles per
+// workgroup (to within one); grid tile g is tile_at(g), so slices keep the
+// 128-byte-aligned tiling.  Compared with k_reduce_persistent, whose loads
+// land in registers, at 8 ranks x 64 MiB on two MI355X boxes, interleaved:
+// 88.0 - 88.4 us against 90.9 - 91.6 us, and 90.1 - 90.7 against 91.7 - 92.0.
+template <int N, Out kOut>
+__global__ __launch_bounds__(kStageBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                     uint32_t tiles_per_slice, uint32_t ntiles) {
+    static_assert(kOut != Out::kAll, "the fan-out keeps the register kernel");
+    PC_STAGE_ARRAYS(N)
+    const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, stride = gridDim.x;
+    for_each_stage_batch([&](auto tiles, uint32_t g0) {
+        constexpr int kTiles = decltype(tiles)::value;
+        StageTile tile[kTiles];
+        uint32_t slice[kTiles];
+#pragma unroll
+        for (int j = 0; j < kTiles; ++j) {
+            const TileAt at = tile_at<kOut>(g0 + j * stride, nslice, tiles_per_slice, kStageTileChunks);
+            tile[j] = {at.first, at.bytes};
+            slice[j] = at.s;
+        }
+        StagedBatch<N, false, kTiles> b{src, tile, {PC_STAGE_LIST}, w, lane};
+        b.run();
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4 * kTiles; ++j) {
+            const StageTile t = tile[j / 4];
+            const __amdgpu_buffer_rsrc_t ro =
+                tile_rsrc(dst.p[kOut == Out::kOne ? 0 : slice[j / 4]] + t.first, t.bytes);
+            store16_tile(ro, stage_row_offset(j, w, lane), b.res[j]);
+        }
+    }, ntiles);
+}
+
 // ---- single-launch twoshot, bandwidth regime: fold, then hand out ---------------
 // Each workgroup first folds its tiles as twoshot phase 1 does, into the
 // owner's output only (N input streams, one output stream), and only then
@@ -318,11 +361,38 @@ static hipError_t go_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                            args, 0, stream);
 }
 
+// The staged kernel serves four or more ranks.  A/B against the register
+// kernel on one MI355X, warm / caches flushed, us: 8 ranks 4.7 / 10.1 vs
+// 5.1-5.7 / 10.7-11.1 at 4 MiB per rank, 17.0 / 22.2 vs 18.4 / 22.5 at 12,
+// 45.2 / 50.5 vs 45.3 / 50.9 at 32, 90.1-90.7 / 93.7-94.5 vs 91.7-92.0 /
+// 96.8-96.9 at 64; 6 ranks 69.8-70.6 vs 71.8-72.2 and 4 ranks 49.7-51.4 vs
+// 51.2-51.4 at 64.  With 2 ranks it lost (29.4 vs 28.5-28.9 warm, 35.7 vs
+// 33.2-33.7 flushed at 64 MiB), so fewer ranks keep the register kernel.
+// Whole rounds of one workgroup per CU, then as few workgroups as give that
+// many rounds, so every workgroup does the same number of tiles (to within
+// one).  The dynamic LDS request keeps a second workgroup off each CU.
+constexpr int kStagedMinRanks = 4;
+template <int N, Out kOut>
+static hipError_t go_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                                   uint32_t slices, hipStream_t stream) {
+    uint32_t tiles_per_slice = slice_tiles(nslice, slices, kStageTileChunks);
+    uint32_t ntiles = tiles_per_slice * slices;
+    const uint32_t cus = device_cus();
+    const uint32_t rounds = (ntiles + cus - 1) / cus;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    void* args[] = {&src, &dst, &nslice, &tiles_per_slice, &ntiles};
+    return hipLaunchKernel((const void*)&k_reduce_staged<N, kOut>, dim3(grid), dim3(kStageBlock), args,
+                           stage_pad_bytes<N>(), stream);
+}
+
 template <int N, Out kOut>
 static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                    uint32_t nslice, uint32_t slices, hipStream_t stream) {
     switch (rg) {
-        case Regime::kStream: return go_reduce_persistent<N, kOut>(src, dst, nslice, slices, stream);
+        case Regime::kStream:
+            if constexpr (kOut == Out::kAll || N < kStagedMinRanks)
+                return go_reduce_persistent<N, kOut>(src, dst, nslice, slices, stream);
+            else return go_reduce_staged<N, kOut>(src, dst, nslice, slices, stream);
         case Regime::kMid: return go_reduce<N, 2, false, kOut>(src, dst, nslice, slices, stream);
         default: return go_reduce<N, 1, false, kOut>(src, dst, nslice, slices, stream);
     }
