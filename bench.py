@@ -37,12 +37,14 @@ HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per launch of the headline kernel from two rocprofv3 counter runs
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
-# copy); profiles/k_reduce_8x64MiB_hbm_counters.md has the commands and
+# copy); profiles/k_reduce_staged_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604522096,
+TRAFFIC = {"bytes": 604666407,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
+                       "collective_datapath_amd/csrc/pc_staged.hpp",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "25af94106e87d985e6e331745034024280a2f1bd0c04f77b2ce97f972287c15a"}
+           "sha256": "339bd0678691cbf41843069fcca8f4e82937559dea5756034dcb89d1c20b0360"}
+HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0>"
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -95,6 +97,23 @@ class Dev:
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
+
+    def per_launch_us(self, fn, launches):
+        """Each of `launches` calls between its own pair of events (after 3
+        untimed calls): median, 10th and 90th percentile in us, and the count."""
+        torch = self.torch
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+        return (statistics.median(t), t[len(t) // 10], t[(9 * len(t)) // 10], len(t))
 
     def graph_us(self, fn, calls=128, replays=8):
         """Per-call us: `calls` calls in one graph, 1 warm replay, `replays` timed."""
@@ -167,48 +186,82 @@ def gbs(nbytes, us):
 
 
 def run_headline(d, B, synth, args, out):
+    """The headline call three ways, all on the same stream:
+      * warm: `--steps` back-to-back calls on one input set (the line's value);
+      * rotated: `--steps` back-to-back calls cycling three distinct input
+        sets of 8 x 64 MiB, so no call finds its inputs in the 256 MiB
+        last-level cache (the previous two calls moved 1.1 GiB through it);
+      * per launch: 1,100 calls, each between its own pair of events; the
+        median is the kernel-time statistic (plus the event overhead).
+    Every output of every input set is checked bit for bit against the
+    oracle, and the oracle is timed on the host cores on the same call."""
+    import dataclasses
+    torch = d.torch
     case = synth.C4_ONESHOT_64M
     log("generating", case.name)
     xs = case.inputs()
-    ins = [d.up(x) for x in xs]
-    res = d.torch.full((case.k,), -1, dtype=d.torch.int16, device=d.dev)
-    fn = lambda: B.pc_reduce(ins, res, case.k)  # noqa: E731
+    # Input sets 1 and 2 hold the same values with the rank order rotated by
+    # one and two places: distinct memory, and different fold results.
+    sets = [[d.up(x) for x in xs]]
+    for j in (1, 2):
+        sets.append([sets[0][(r + j) % case.n].clone() for r in range(case.n)])
+    host_sets = [[xs[(r + j) % case.n] for r in range(case.n)] for j in range(3)]
+    res = [torch.full((case.k,), -1, dtype=torch.int16, device=d.dev) for _ in range(3)]
+    nbytes = case.bytes_moved()
+    fn = lambda: B.pc_reduce(sets[0], res[0], case.k)  # noqa: E731
     log("timing headline:", args.steps, "calls after", args.warmup, "warm-up")
     ms = d.events_ms(fn, args.steps, args.warmup)
+    turn = [0]
+
+    def rotated():
+        j = turn[0] % 3
+        turn[0] += 1
+        B.pc_reduce(sets[j], res[j], case.k)
+    ms_rot = d.events_ms(rotated, 3 * max(1, args.steps // 3), 3)
+    med_us, p10_us, p90_us, count = d.per_launch_us(fn, 1100)
     g_us = d.graph_us(fn, calls=16, replays=4)
-    nbytes = case.bytes_moved()
     ach = gbs(nbytes, ms * 1000.0)
     out["headline"] = {"workload": case.name, "bytes_per_call": nbytes,
-                       "event_us_per_launch": round(ms * 1e3, 3), "graph_us": round(g_us, 3),
-                       "gbs": round(ach, 1)}
-    got = d.down(res, np.uint16)
+                       "event_us_per_launch": round(ms * 1e3, 3), "gbs": round(ach, 1),
+                       "rotated_inputs": {"sets": 3, "event_us_per_launch": round(ms_rot * 1e3, 3),
+                                          "gbs": round(gbs(nbytes, ms_rot * 1e3), 1),
+                                          "frac_of_hbm_peak": round(gbs(nbytes, ms_rot * 1e3) / HBM_PEAK_GBS, 4)},
+                       "per_launch_events": {"launches": count, "median_us": round(med_us, 3),
+                                             "p10_us": round(p10_us, 3), "p90_us": round(p90_us, 3),
+                                             "gbs_at_median": round(gbs(nbytes, med_us), 1)},
+                       "graph_us": round(g_us, 3)}
+    got = [d.down(r, np.uint16) for r in res]
     if not args.no_parity or not args.no_cpu_baseline:
         import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
-        # About 10 s of oracle work: the full headline call repeated, median.
-        runs = []
-        want = None
-        t_end = time.perf_counter() + 10.0
-        while len(runs) < 3 or (time.perf_counter() < t_end and len(runs) < 500):
-            t0 = time.perf_counter()
-            want = oracle.reduce(xs, threads=threads)
-            runs.append(time.perf_counter() - t0)
-        t0 = time.perf_counter()
-        oracle.reduce([x[: case.k // 16] for x in xs], threads=1)
-        single = (time.perf_counter() - t0) * 16
-        med = statistics.median(runs)
+
+        def median_of(fn_cpu, runs, seconds):
+            fn_cpu()                                   # warm-up, not counted
+            times = []
+            t_end = time.perf_counter() + seconds
+            while len(times) < runs or (time.perf_counter() < t_end and len(times) < 200):
+                t0 = time.perf_counter()
+                fn_cpu()
+                times.append(time.perf_counter() - t0)
+            return statistics.median(times), len(times)
+        wants = [oracle.reduce(h, threads=threads) for h in host_sets]
+        med, nrun = median_of(lambda: oracle.reduce(xs, threads=threads), 5, 8.0)
+        med1, nrun1 = median_of(lambda: oracle.reduce(xs, threads=1), 5, 0.0)
         out["cpu_baseline"] = {
             "value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the full headline call (8 x 64 MiB in, 64 MiB out), repeated for about 10 s: "
-                      f"median of {len(runs)} runs, {threads} threads split by element range; "
-                      f"single-thread estimate "
-                      f"{nbytes / single / 1e9:.3f} GB/s from 1/16 of the elements",
+            "sample": f"the full headline call (8 x 64 MiB in, 64 MiB out): median of {nrun} runs after "
+                      f"1 warm-up on {threads} threads split by element range; single-threaded, median of "
+                      f"{nrun1} full runs after 1 warm-up: {nbytes / med1 / 1e9:.3f} GB/s",
             "ms": round(med * 1e3, 2),
+            "single_thread": {"value": round(nbytes / med1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "ms": round(med1 * 1e3, 1), "runs": nrun1},
             "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
         if not args.no_parity:
-            ok = bool(np.array_equal(got, want))
+            ok = all(bool(np.array_equal(g, w)) for g, w in zip(got, wants))
             out.setdefault("parity", {})["headline"] = ok
-            log("headline parity", ok)
+            log("headline parity (3 input sets)", ok)
+    del sets, res
+    torch.cuda.empty_cache()
     return ms, ach
 
 
@@ -222,6 +275,8 @@ def kernel_sources_sha256():
 
 
 def measured_traffic():
+    if TRAFFIC["bytes"] is None:
+        return None
     return TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sha256"] else None
 
 
@@ -413,6 +468,19 @@ def run_hbm_regime(d, B, synth, oracle, args, out):
     def ev_us(fn, reps=20):
         return d.events_ms(fn, reps, 3) * 1e3
 
+    def isolated_us(setup, fn, reps):
+        """Mean us of `fn` alone: `setup` runs untimed before each call."""
+        total = 0.0
+        for _ in range(reps):
+            setup()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            total += a.elapsed_time(b) * 1000.0
+        return total / reps
+
     idx_np = np.concatenate([np.arange(0, 4096), np.arange(k - 4096, k),
                              np.random.default_rng(64).integers(0, k, 1 << 14)])
     idx = torch.from_numpy(idx_np).to(d.dev)
@@ -473,11 +541,26 @@ def run_hbm_regime(d, B, synth, oracle, args, out):
         publish_all()
         B.pc_consume_sentinel(slots, res, k, bms)
     us_publish = ev_us(publish_all, 10)
+    us_isolated = isolated_us(publish_all, lambda: B.pc_consume_sentinel(slots, res, k, bms), 10)
     us = ev_us(cycle, 10) - us_publish             # the cycle runs last: slots end re-armed
     ok = oracle is not None and np.array_equal(
         d.down(res[idx], np.uint16), oracle.reduce([oracle.publish_sentinel(x) for x in xs])) and \
         bool((bms == -1).all()) and bool((slots[n - 1][idx] == -1).all())
-    row("consume_sentinel", n * 2 * k + 2 * k + n * 2 * k + k // 64, us, ok)
+    sbytes = n * 2 * k + 2 * k + n * 2 * k + k // 64
+    row("consume_sentinel", sbytes, us, ok)
+    rows["consume_sentinel"]["timing"] = "publish-and-consume cycles minus publish-only runs"
+    rows["consume_sentinel"]["isolated"] = {
+        "timing": "slots published (untimed), then the consume alone between two events; mean of 10",
+        "event_us_per_call": round(us_isolated, 2), "gbs": round(gbs(sbytes, us_isolated), 1),
+        "frac_of_hbm_peak": round(gbs(sbytes, us_isolated) / HBM_PEAK_GBS, 4)}
+    # Write-only reference on the same eight 64 MiB slots: torch's fill
+    # kernel, back to back.  The re-arm pass of the consume (all packs
+    # ready) writes exactly these bytes.
+    us_fill = ev_us(lambda: [t.fill_(-1) for t in slots], 10)
+    rows["write_only_reference"] = {
+        "workload": "torch fill_ of 8 x 64 MiB (the bytes a full re-arm writes)",
+        "event_us_per_launch": round(us_fill, 2), "bytes_per_call": n * 2 * k,
+        "gbs": round(gbs(n * 2 * k, us_fill), 1), "frac_of_hbm_peak": round(gbs(n * 2 * k, us_fill) / HBM_PEAK_GBS, 4)}
     del slots
     # Speculative reduce, one flag per 8192 elements, all flags current.
     flags = [torch.full((k // 8192,), 5, dtype=torch.int32, device=d.dev) for _ in range(n)]
@@ -699,7 +782,7 @@ def main():
         line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(),
-                            "kernel": "pcdp::k_reduce_persistent<8, (pcdp::Out)0>"}
+                            "kernel": HEADLINE_KERNEL}
     if "cpu_baseline" in out:
         line["cpu_baseline"] = out.pop("cpu_baseline")
     line["parity_ok"] = bool(out["parity"]) and all(out["parity"].values())
