@@ -435,8 +435,8 @@ def run_c3(d, B, synth, oracle, args, out):
         onev = d.down(one, np.uint16)
     # Two launches (slice reduce, then copy-out), the single-launch form, and
     # the single launch whose phases are linked per tile by epoch flags.
-    ws = d.torch.zeros(B.pc_twoshot_linked_workspace_bytes(case.n, case.k) // 4,
-                       dtype=d.torch.int32, device=d.dev)
+    ws = d.torch.zeros(B.pc_twoshot_linked_workspace_bytes(case.n, case.k) // 8,
+                       dtype=d.torch.int64, device=d.dev)
     linked = lambda i, o, k: B.pc_twoshot_linked(i, o, k, ws)  # noqa: E731
     for name, fn, nbytes in (("twoshot_1m", B.pc_twoshot, 2 * case.k * (2 * case.n + 1)),
                              ("twoshot_fused_1m", B.pc_twoshot_fused, 2 * case.k * 2 * case.n),
@@ -496,7 +496,7 @@ def run_hbm_regime(d, B, synth, oracle, args, out):
             out["parity"]["hbm_" + name] = bool(ok)
 
     outs = [torch.empty(k, dtype=torch.int16, device=d.dev) for _ in range(n)]
-    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4, dtype=torch.int32, device=d.dev)
+    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8, dtype=torch.int64, device=d.dev)
     for name, fn, units in (("twoshot", lambda: B.pc_twoshot(ins, outs, k), 2 * n + 1),
                             ("twoshot_fused", lambda: B.pc_twoshot_fused(ins, outs, k), 2 * n),
                             ("twoshot_linked", lambda: B.pc_twoshot_linked(ins, outs, k, ws), 2 * n + 1)):
@@ -658,8 +658,8 @@ def run_sweep(d, B, synth, oracle, args, out):
                 moved = 2 * n * nbytes
             else:
                 outs = [d.torch.empty(k, dtype=d.torch.int16, device=d.dev) for _ in range(n)]
-                ws = d.torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4,
-                                   dtype=d.torch.int32, device=d.dev)
+                ws = d.torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8,
+                                   dtype=d.torch.int64, device=d.dev)
                 fn = lambda: B.pc_twoshot_linked(ins, outs, k, ws)  # noqa: E731
                 moved = (2 * n + 1) * nbytes
             t = timing(d, fn, 500, 50)

@@ -26,12 +26,14 @@ PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
 EXPORTS = ("pc_copy", "pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
+           "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes",
+           "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated", "pc_strerror", "pc_abi_version")
-PC_ABI_VERSION = 6          # the include/pc.h this binding is written against
+PC_ABI_VERSION = 7          # the include/pc.h this binding is written against
 PC_MAX_ATTEMPTS = 65536
 PC_LINKED_GROUPS = 256
-PC_LINKED_STATUS_WORD = 256
+PC_LINKED_STATUS_WORD = 256       # uint64 words
+PC_LINKED_POLL_LIMIT_WORD = 257   # uint64 words
 PC_SENTINEL = 0xFFFF
 
 if not os.path.exists(LIB_PATH):
@@ -77,8 +79,8 @@ _lib.pc_publish_sentinel.argtypes = [_P, _P, _S, _P]
 _lib.pc_reduce_validated.argtypes = [_P, _P, _I, _P, _S, _S, ctypes.c_uint32, ctypes.c_uint32, _P, _P]
 _lib.pc_consume_sentinel.argtypes = [_P, _I, _P, _S, _P, _P]
 for _f in ("pc_copy", "pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_twoshot_linked", "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
-           "pc_reduce_validated"):
+           "pc_twoshot_linked", "pc_allgather_copy", "pc_publish_sentinel",
+           "pc_consume_sentinel", "pc_reduce_validated"):
     getattr(_lib, _f).restype = _I
 _lib.pc_strerror.argtypes = [_I]
 _lib.pc_strerror.restype = ctypes.c_char_p
@@ -234,8 +236,8 @@ def pc_twoshot_linked(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, 
                       workspace_bytes: Optional[int] = None, stream=None, check: bool = True) -> int:
     """Twoshot in one launch, phases linked per tile by epoch flags kept in
     `workspace` (include/pc.h, pc_twoshot_linked).
-    `workspace`: zero-filled before its first use, then reused unchanged
-    across calls.  `workspace_bytes` defaults to the size of a workspace
+    `workspace`: zero-filled before its first use (uint64 words; a torch
+    int64 tensor), then reused unchanged across calls.  `workspace_bytes` defaults to the size of a workspace
     tensor and must be given for a raw address."""
     if len(outs) != len(inputs):
         raise ValueError("pc_twoshot_linked needs one output per input")

@@ -2,7 +2,9 @@
 
 Every source under csrc/ is compiled by its own hipcc process (in parallel)
 into collective_datapath_amd/_build/, and the objects are linked into
-collective_datapath_amd/libpcdp.so.  The sources share no device symbols, so
+collective_datapath_amd/libpcdp.so.  A second library, libpcdp_delay.so,
+differs only in the flag-linked twoshot, built with injected pseudo-random
+delays; only the tests load it.  The sources share no device symbols, so
 no relocatable device code is needed.  Flags that matter for bit-exactness:
 no fast-math, no fp contraction, and fp32 subnormals kept on the device.
 Packed-fp32 instruction selection is switched off (plain v_add_f32 per
@@ -21,6 +23,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpcdp.so")
+DELAY_LIB = os.path.join(HERE, "libpcdp_delay.so")  # test-only variant, see build()
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -52,13 +55,24 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
         obj = os.path.join(OBJ_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
         objs.append(obj)
         jobs.append([hipcc, *HIPCC_FLAGS, *extra_flags, inc, "-c", src, "-o", obj])
+    # The test-only delay-stress build of the flag-linked twoshot: the same
+    # library with pc_linked.hip compiled with PC_LINKED_DELAY_STRESS.
+    linked_src = os.path.join(CSRC, "pc_linked.hip")
+    delay_obj = os.path.join(OBJ_DIR, "pc_linked_delay.o")
+    jobs.append([hipcc, *HIPCC_FLAGS, *extra_flags, "-DPC_LINKED_DELAY_STRESS", inc, "-c", linked_src,
+                 "-o", delay_obj])
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=workers) as pool:
         for f in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
             f.result()
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC"]
     tmp = out + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([*link, *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
+    delay_objs = [delay_obj if o.endswith(os.sep + "pc_linked.o") else o for o in objs]
+    tmp = DELAY_LIB + ".tmp"
+    _run([*link, *delay_objs, "-o", tmp], verbose)
+    os.replace(tmp, DELAY_LIB)
     return out
 
 

@@ -165,15 +165,16 @@ pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t* const
 
 static_assert(PC_LINKED_GROUPS == pcdp::kLinkGroups, "fixed grid of the linked twoshot");
 static_assert(PC_LINKED_STATUS_WORD == pcdp::kLinkGroups, "status word follows the counters");
+static_assert(PC_LINKED_POLL_LIMIT_WORD == pcdp::kLinkGroups + 1, "poll limit follows the status word");
 
 size_t pc_twoshot_linked_workspace_bytes(int n, size_t k) {
     if (!valid_n(n) || k > PC_MAX_ELEMS || k % (8 * (size_t)n)) return 0;
     const size_t tiles = k ? pcdp::linked_tiles(n, k / 8 / (size_t)n) : 0;
-    return sizeof(uint32_t) * (pcdp::kLinkGroups + pcdp::kLinkHeaderWords + tiles);
+    return sizeof(uint64_t) * (pcdp::kLinkGroups + pcdp::kLinkHeaderWords + tiles);
 }
 
 pc_status pc_twoshot_linked(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
-                            uint32_t* workspace, size_t workspace_bytes, void* stream) {
+                            uint64_t* workspace, size_t workspace_bytes, void* stream) {
     const void* src[PC_MAX_RANKS];
     void* dst[PC_MAX_RANKS];
     bool empty;
@@ -187,7 +188,7 @@ pc_status pc_twoshot_linked(const uint16_t* const* inputs, int n, uint16_t* cons
     for (int r = 0; r < n; ++r)
         if (overlaps(workspace, need, inputs[r], bytes) || overlaps(workspace, need, outs[r], bytes))
             return PC_EINVAL;
-    const hipError_t e = pcdp::launch_twoshot_linked(src, n, dst, k / 8 / (size_t)n, workspace,
+    const hipError_t e = pcdp::launch_twoshot_linked(src, n, dst, k / 8 / (size_t)n, workspace, nullptr,
                                                      static_cast<hipStream_t>(stream));
     return e == hipErrorCooperativeLaunchTooLarge ? PC_EUNSUPPORTED : from_hip(e);
 }

@@ -34,15 +34,17 @@ hipError_t launch_twoshot_fused(const void* const* src, int n, void* const* outs
                                 size_t nchunks_slice, hipStream_t stream);
 
 // Flag-linked single-launch twoshot on a fixed grid of kLinkGroups
-// workgroups.  The workspace holds kLinkGroups call counters, a header of
-// kLinkHeaderWords words (word 0: give-up count) and linked_tiles() flags.
-// Returns hipErrorCooperativeLaunchTooLarge, launching nothing, when the grid
-// cannot be resident on the device at once.
+// workgroups.  The workspace holds kLinkGroups 64-bit call counters, a
+// header of kLinkHeaderWords 64-bit words (word 0: give-up count, word 1:
+// poll limit, 0 = default) and linked_tiles() 64-bit flags.  Abandoned
+// waits are counted at `status` (NULL: the workspace's header word 0).
+// Returns hipErrorCooperativeLaunchTooLarge, launching nothing, when the
+// grid cannot be resident on the device at once.
 constexpr uint32_t kLinkGroups = 256;
 constexpr uint32_t kLinkHeaderWords = 64;
 size_t linked_tiles(int n, size_t nchunks_slice);
 hipError_t launch_twoshot_linked(const void* const* src, int n, void* const* outs,
-                                 size_t nchunks_slice, void* workspace, hipStream_t stream);
+                                 size_t nchunks_slice, void* workspace, void* status, hipStream_t stream);
 
 // LL lines: 16-byte chunks of src -> 4 lines each.
 hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t seq,

@@ -14,16 +14,17 @@
 // and that epoch is the value a producer writes to signal readiness) and
 // Section 3.2 (the consumer waits on the notification, then moves the data).
 //
-// Workspace (caller-owned, zero before its first use, uint32 words):
+// Workspace (caller-owned, zero before its first use, uint64 words):
 //   [0, G)          call counter of workgroup w (G = kLinkGroups)
 //   [G]             number of tiles whose wait gave up (sticky)
+//   [G + 1]         polls per wait before giving up; 0 = kMaxPolls
 //   [G + 64, ...)   flag of tile t: the epoch of the call that last
 //                   finished reducing it
 // Workgroup w runs call number ctr[w] + 1 as its epoch and stores it back
 // when it is done.  Every call launches all G workgroups, so all counters
 // agree and a stale flag (an earlier epoch, or zero) never equals the
 // current one; no flag has to be cleared between calls, and a graph replay
-// advances the epoch by itself.
+// advances the epoch by itself.  Epochs are 64-bit, so they never wrap.
 //
 // Tile t = (slice s, tile j of the slice) covers up to 256*U chunks of 16
 // bytes of slice s.  Phase 1: workgroup t mod G folds tile t from the n
@@ -36,6 +37,20 @@
 // launch), so every awaited flag is eventually published.  The wait is
 // still bounded: a workgroup that gives up adds the number of its tiles to
 // the status word and skips them, so the kernel always ends.
+//
+// Measured floor (one MI355X, 8 ranks, per call inside a graph): the
+// cross-workgroup hand-off costs more than a kernel boundary.  At 8 KiB per
+// rank this kernel takes 4.6 us, 4.2 us with its fences removed (timing
+// only), against 3.5 us for the two-launch form and 1.9 us for the
+// single-launch form without flags; at 1 MiB, 8.0 / 6.8 against 4.9 / 3.4.
+// A grid sized to the tile count with one device epoch advanced by the last
+// workgroup to finish was slower still (5.0 us at 8 KiB, 8.9 at 1 MiB).
+//
+// Built with PC_LINKED_DELAY_STRESS defined (a test-only variant), every
+// wave sleeps a pseudo-random time, seeded by workgroup, wave and epoch,
+// before its phase-1 stores, before the flags are published and before its
+// phase-2 reads, so that the flag hand-off is exercised at timings the
+// natural schedule does not produce.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 
@@ -45,23 +60,45 @@ namespace pcdp {
 
 constexpr int kLinkBlock = 256;
 constexpr uint32_t kMaxPolls = 1u << 20;
+constexpr uint32_t kLinkPollLimitWord = 1;  // after the status word
+
+// Pseudo-random sleep of up to ~0.15 ms in the stress variant; nothing
+// otherwise.
+__device__ __forceinline__ void stress_delay(uint64_t epoch, uint32_t who, uint32_t where) {
+#ifdef PC_LINKED_DELAY_STRESS
+    uint32_t x = (uint32_t)epoch * 0x9E3779B1u ^ who * 0x85EBCA77u ^ where * 0xC2B2AE3Du;
+    x ^= x >> 15;
+    x *= 0x2C1B3C6Du;
+    x ^= x >> 13;
+    for (uint32_t i = x % 48u; i; --i) __builtin_amdgcn_s_sleep(127);
+#else
+    (void)epoch;
+    (void)who;
+    (void)where;
+#endif
+}
 
 template <int N, int U, bool kStream, bool kNtCopies>
 __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*> src,
-                                                                Ptrs<u32x4*> outs, uint32_t* ws,
+                                                                Ptrs<u32x4*> outs, uint64_t* ws,
+                                                                uint64_t* status,
                                                                 size_t slice_chunks,
                                                                 size_t tiles_per_slice) {
     constexpr uint32_t kTile = kLinkBlock * U;  // chunks per tile
     constexpr int kLoadPolicy = kStream ? kPolicyNonTemporal : 0;
-    __shared__ uint32_t shared_epoch, ready;
+    __shared__ uint64_t shared_epoch;
+    __shared__ uint32_t shared_limit, ready;
     const uint32_t w = blockIdx.x, tid = threadIdx.x;
-    uint32_t* const ctr = ws;
-    uint32_t* const status = ws + kLinkGroups;
-    uint32_t* const flags = ws + kLinkGroups + kLinkHeaderWords;
+    uint64_t* const ctr = ws;
+    uint64_t* const flags = ws + kLinkGroups + kLinkHeaderWords;
 
-    if (tid == 0) shared_epoch = ctr[w] + 1u;
+    if (tid == 0) {
+        shared_epoch = ctr[w] + 1u;
+        const uint64_t limit = ws[kLinkGroups + kLinkPollLimitWord];
+        shared_limit = limit == 0 || limit > kMaxPolls ? kMaxPolls : (uint32_t)limit;
+    }
     __syncthreads();
-    const uint32_t epoch = shared_epoch;
+    const uint64_t epoch = shared_epoch;
     const size_t ntiles = (size_t)N * tiles_per_slice;
 
     // ---- phase 1: fold this workgroup's owner tiles, then publish them -----------
@@ -83,12 +120,14 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
                 for (int u = 0; u < U; ++u)
                     v[u][r] = load16_rsrc<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
             }
+            stress_delay(epoch, w * 4 + tid / kWave, (uint32_t)t);
             const __amdgpu_buffer_rsrc_t ro = tile_rsrc(outs.p[s] + c0, bytes);
 #pragma unroll
             for (int u = 0; u < U; ++u) store16_tile(ro, (u * kLinkBlock + tid) * 16u, fold_chunk<N>(v[u]));
         }
         __syncthreads();
         if (tid == 0) {
+            stress_delay(epoch, w, 0x10000u);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             for (size_t t = w; t < ntiles; t += kLinkGroups)
                 __hip_atomic_store(flags + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -102,13 +141,14 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
     const size_t first = (w + kLinkGroups / 2) % kLinkGroups;
     if (first < ntiles) {
         if (tid == 0) {
+            const uint32_t limit = shared_limit;
             bool ok = true;
-            uint32_t mine = 0;
+            uint64_t mine = 0;
             for (size_t t = first; t < ntiles; t += kLinkGroups) {
                 ++mine;
                 uint32_t polls = 0;
                 while (ok && __hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-                    if (++polls >= kMaxPolls) ok = false;
+                    if (++polls >= limit) ok = false;
                     else __builtin_amdgcn_s_sleep(1);
                 }
             }
@@ -118,6 +158,7 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
         }
         __syncthreads();
         if (ready) {
+            stress_delay(epoch, w * 4 + tid / kWave, 0x20000u);
             for (size_t t = first; t < ntiles; t += kLinkGroups) {
                 const size_t s = t / tiles_per_slice;
                 const SliceTile st = slice_tile((uint32_t)s, (uint32_t)(t % tiles_per_slice), slice_chunks, kTile);
@@ -172,8 +213,8 @@ static hipError_t resident_capacity(const void* kernel, int* capacity) {
 }
 
 template <int N, int U, bool kStream, bool kNtCopies>
-static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint32_t* ws, size_t slice_chunks,
-                            hipStream_t stream) {
+static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint64_t* ws, uint64_t* status,
+                            size_t slice_chunks, hipStream_t stream) {
     const void* kernel = (const void*)&k_twoshot_linked<N, U, kStream, kNtCopies>;
     // 0 = not yet known, else capacity + 1, per device.
     static std::atomic<int> known[64];
@@ -188,43 +229,44 @@ static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint32_t* ws, 
     }
     if (cap < (int)kLinkGroups) return hipErrorCooperativeLaunchTooLarge;
     size_t tiles_per_slice = slice_tiles(slice_chunks, N, kLinkBlock * U);
-    void* args[] = {&s, &o, &ws, &slice_chunks, &tiles_per_slice};
+    void* args[] = {&s, &o, &ws, &status, &slice_chunks, &tiles_per_slice};
     return hipLaunchKernel(kernel, dim3(kLinkGroups), dim3(kLinkBlock), args, 0, stream);
 }
 
 template <int N>
-static hipError_t go_linked_n(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint32_t* ws, size_t slice_chunks,
-                              hipStream_t stream) {
+static hipError_t go_linked_n(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint64_t* ws, uint64_t* status,
+                              size_t slice_chunks, hipStream_t stream) {
     // From 48 MiB per rank the copies carry the non-temporal hint: at 8 ranks
     // 195 vs 218 us at 64 MiB per rank, 286 vs 333 us at 96 MiB and 149 vs
     // 153 us at 48 MiB; below it the default policy is 1-3% faster.
     if (slice_chunks * N * 16 >= ((size_t)48 << 20))
-        return go_linked<N, 4, true, true>(s, o, ws, slice_chunks, stream);
+        return go_linked<N, 4, true, true>(s, o, ws, status, slice_chunks, stream);
     switch (linked_unroll(slice_chunks, N)) {
-        case 1: return go_linked<N, 1, false, false>(s, o, ws, slice_chunks, stream);
-        case 2: return go_linked<N, 2, false, false>(s, o, ws, slice_chunks, stream);
-        default: return go_linked<N, 4, true, false>(s, o, ws, slice_chunks, stream);
+        case 1: return go_linked<N, 1, false, false>(s, o, ws, status, slice_chunks, stream);
+        case 2: return go_linked<N, 2, false, false>(s, o, ws, status, slice_chunks, stream);
+        default: return go_linked<N, 4, true, false>(s, o, ws, status, slice_chunks, stream);
     }
 }
 
 hipError_t launch_twoshot_linked(const void* const* src, int n, void* const* outs,
-                                 size_t nchunks_slice, void* workspace, hipStream_t stream) {
+                                 size_t nchunks_slice, void* workspace, void* status, hipStream_t stream) {
     Ptrs<const u32x4*> s;
     Ptrs<u32x4*> o;
     for (int r = 0; r < kMaxRanks; ++r) {
         s.p[r] = r < n ? static_cast<const u32x4*>(src[r]) : nullptr;
         o.p[r] = r < n ? static_cast<u32x4*>(outs[r]) : nullptr;
     }
-    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    uint64_t* ws = static_cast<uint64_t*>(workspace);
+    uint64_t* st = status ? static_cast<uint64_t*>(status) : ws + kLinkGroups;
     switch (n) {
-        case 1: return go_linked_n<1>(s, o, ws, nchunks_slice, stream);
-        case 2: return go_linked_n<2>(s, o, ws, nchunks_slice, stream);
-        case 3: return go_linked_n<3>(s, o, ws, nchunks_slice, stream);
-        case 4: return go_linked_n<4>(s, o, ws, nchunks_slice, stream);
-        case 5: return go_linked_n<5>(s, o, ws, nchunks_slice, stream);
-        case 6: return go_linked_n<6>(s, o, ws, nchunks_slice, stream);
-        case 7: return go_linked_n<7>(s, o, ws, nchunks_slice, stream);
-        case 8: return go_linked_n<8>(s, o, ws, nchunks_slice, stream);
+        case 1: return go_linked_n<1>(s, o, ws, st, nchunks_slice, stream);
+        case 2: return go_linked_n<2>(s, o, ws, st, nchunks_slice, stream);
+        case 3: return go_linked_n<3>(s, o, ws, st, nchunks_slice, stream);
+        case 4: return go_linked_n<4>(s, o, ws, st, nchunks_slice, stream);
+        case 5: return go_linked_n<5>(s, o, ws, st, nchunks_slice, stream);
+        case 6: return go_linked_n<6>(s, o, ws, st, nchunks_slice, stream);
+        case 7: return go_linked_n<7>(s, o, ws, st, nchunks_slice, stream);
+        case 8: return go_linked_n<8>(s, o, ws, st, nchunks_slice, stream);
         default: return hipErrorInvalidValue;
     }
 }

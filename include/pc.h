@@ -74,7 +74,7 @@ enum {
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 6
+#define PC_ABI_VERSION 7
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -211,31 +211,38 @@ PC_API pc_status pc_twoshot_fused(const uint16_t* const* inputs, int n, uint16_t
  *   workspace : device, 16-byte aligned, at least
  *               pc_twoshot_linked_workspace_bytes(n, k) bytes, owned by the
  *               caller.  It must be zero-filled before its first use and then
- *               left to the library: it carries one call counter per
+ *               left to the library: it carries one 64-bit call counter per
  *               workgroup of a fixed grid of PC_LINKED_GROUPS workgroups, so
  *               successive calls (and graph replays) need no host-side epoch
- *               and no clearing.  A workspace serves any n and k it is large
- *               enough for.  Two calls that may run at the same time (other
- *               streams) need separate workspaces; it must not overlap any
- *               input or output.
- *   workspace[PC_LINKED_STATUS_WORD] : the number of tiles, summed over all
- *               calls, whose wait for a flag was abandoned after a bounded
- *               number of polls (their outputs are then incomplete).  It
- *               stays 0 while the grid is resident, which is checked before
- *               launch.
+ *               and no clearing.  Epochs are 64-bit and never wrap.  A
+ *               workspace serves any n and k it is large enough for.  Two
+ *               calls that may run at the same time (other streams) need
+ *               separate workspaces; it must not overlap any input or output.
+ *   workspace[PC_LINKED_STATUS_WORD] (uint64) : the number of tiles, summed
+ *               over all calls, whose wait for a flag was abandoned after a
+ *               bounded number of polls; the copies of those tiles into the
+ *               non-owner outputs are then skipped (those bytes of outs[r],
+ *               r != s, are left as they were), while every owner output
+ *               outs[s] is complete.  It stays 0 while the grid is resident,
+ *               which is checked before launch.
+ *   workspace[PC_LINKED_POLL_LIMIT_WORD] (uint64) : polls per wait before it
+ *               is abandoned; 0 (the zero-filled default) or anything above
+ *               2^20 means 2^20.  The caller may set it between calls (a
+ *               diagnostic knob: tests use it to reach the give-up path fast).
  * Errors: PC_EINVAL (also: NULL workspace, workspace_bytes too small,
  * workspace overlapping a buffer), PC_EALIGN, PC_EUNSUPPORTED (the device
  * cannot hold PC_LINKED_GROUPS of these workgroups at once), PC_EHIP.
  */
 #define PC_LINKED_GROUPS 256
-#define PC_LINKED_STATUS_WORD 256
+#define PC_LINKED_STATUS_WORD 256     /* index in uint64 words */
+#define PC_LINKED_POLL_LIMIT_WORD 257 /* index in uint64 words */
 
 /* Workspace bytes pc_twoshot_linked needs for (n, k); 0 if n or k would be
  * rejected by it.  For k == 0 it is the fixed part of the workspace. */
 PC_API size_t pc_twoshot_linked_workspace_bytes(int n, size_t k);
 
 PC_API pc_status pc_twoshot_linked(const uint16_t* const* inputs, int n, uint16_t* const* outs,
-                                   size_t k, uint32_t* workspace, size_t workspace_bytes,
+                                   size_t k, uint64_t* workspace, size_t workspace_bytes,
                                    void* stream);
 
 /*

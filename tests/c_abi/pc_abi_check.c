@@ -105,7 +105,7 @@ static void check_reduce_exact_sums(void) {
     for (int r = 0; r < 4; ++r) outs[r] = dev_alloc(k * 2);
     const size_t ws_bytes = pc_twoshot_linked_workspace_bytes(4, k);
     EXPECT(ws_bytes > 0, "linked workspace size");
-    uint32_t* ws = dev_alloc(ws_bytes);
+    uint64_t* ws = dev_alloc(ws_bytes);
     HIP_OK(hipMemset(ws, 0, ws_bytes));
     for (int form = 0; form < 3; ++form) {
         for (int r = 0; r < 4; ++r) HIP_OK(hipMemset(outs[r], 0xFF, k * 2));
@@ -119,8 +119,8 @@ static void check_reduce_exact_sums(void) {
             EXPECT(all16(h, k, 0x3FA0), "twoshot exact sum in every output");
         }
     }
-    uint32_t status = 1;
-    HIP_OK(hipMemcpy(&status, ws + PC_LINKED_STATUS_WORD, 4, hipMemcpyDeviceToHost));
+    uint64_t status = 1;
+    HIP_OK(hipMemcpy(&status, ws + PC_LINKED_STATUS_WORD, 8, hipMemcpyDeviceToHost));
     EXPECT(status == 0, "linked twoshot abandoned no wait");
 
     for (int r = 0; r < 4; ++r) HIP_OK(hipFree(outs[r]));

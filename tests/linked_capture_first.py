@@ -21,7 +21,7 @@ def main():
     xs = [synth.normal_bf16(1800, 0, r, k) for r in range(n)]
     ins = [torch.from_numpy(x.view(np.int16)).to("cuda:0") for x in xs]
     outs = [torch.empty(k, dtype=torch.int16, device="cuda:0") for _ in range(n)]
-    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4, dtype=torch.int32, device="cuda:0")
+    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8, dtype=torch.int64, device="cuda:0")
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -39,7 +39,7 @@ def main():
         torch.cuda.synchronize()
         for o in outs:
             assert np.array_equal(o.cpu().numpy().view(np.uint16), want), rep
-        w = ws.cpu().numpy().view(np.uint32)
+        w = ws.cpu().numpy().view(np.uint64)
         assert np.all(w[:B.PC_LINKED_GROUPS] == rep + 1) and w[B.PC_LINKED_STATUS_WORD] == 0, rep
     print("OK", flush=True)
 

@@ -133,22 +133,22 @@ def linked_need(n, k):
 
 
 def test_linked_workspace_bytes():
-    fixed = 4 * (B.PC_LINKED_GROUPS + 64)
+    fixed = 8 * (B.PC_LINKED_GROUPS + 64)   # uint64 words
     assert linked_need(8, 0) == fixed
     # 1 MiB per rank, n = 8: slices of 8192 chunks, 512-chunk tiles -> 128 tiles.
-    assert linked_need(8, 8 * 65536) == fixed + 4 * 128
+    assert linked_need(8, 8 * 65536) == fixed + 8 * 128
     # 256 KiB per rank: 256-chunk tiles -> 8 slices of 8 tiles.
-    assert linked_need(8, 8 * 16384) == fixed + 4 * 64
+    assert linked_need(8, 8 * 16384) == fixed + 8 * 64
     # A ragged slice rounds its tile count up: 3 slices of 257 chunks -> 2 tiles each.
-    assert linked_need(3, 3 * 8 * 257) == fixed + 4 * 6
+    assert linked_need(3, 3 * 8 * 257) == fixed + 8 * 6
     # Tiles lie on a grid of 8-chunk (128-byte) lines of the buffer.  Two
     # slices of 509 chunks: slice 1 starts 5 chunks into a line, so its tiles
     # cover [509, 760), [760, 1016) and [1016, 1018) -> 3 tiles per slice.
-    assert linked_need(2, 2 * 8 * 509) == fixed + 4 * 2 * 3
+    assert linked_need(2, 2 * 8 * 509) == fixed + 8 * 2 * 3
     # Slices that start on a line keep ceil(chunks / tile) tiles: 2 x 512.
-    assert linked_need(2, 2 * 8 * 512) == fixed + 4 * 2 * 2
+    assert linked_need(2, 2 * 8 * 512) == fixed + 8 * 2 * 2
     # From 4 MiB per rank the tiles hold 1024 chunks: 8 slices of 32768 chunks.
-    assert linked_need(8, 1 << 21) == fixed + 4 * 8 * 32
+    assert linked_need(8, 1 << 21) == fixed + 8 * 8 * 32
     for bad in [(0, 64), (9, 72), (4, 8 * 4 + 8), (2, (1 << 34) + 16)]:
         assert linked_need(*bad) == 0
 
@@ -268,3 +268,4 @@ def test_binding_rejects_host_and_short_tensors():
 ])
 def test_copy_validation(args, want):
     assert B.pc_copy(stream=0, check=False, **args) == want
+

@@ -18,7 +18,21 @@ from hypothesis import strategies as st  # noqa: E402
 
 from collective_datapath_amd import binding as B  # noqa: E402
 
-pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+
+
+def hip_device_count():
+    """Devices the HIP runtime the library uses can see (torch's view can
+    differ, e.g. a CPU-only torch on a GPU machine)."""
+    import ctypes
+    runtimes = sorted(B._hip_runtimes())
+    if not runtimes:
+        return 0
+    count = ctypes.c_int(0)
+    status = ctypes.CDLL(runtimes[0]).hipGetDeviceCount(ctypes.byref(count))
+    return count.value if status == 0 else 0
+
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available() or hip_device_count() > 0,
                                 reason="valid calls would launch on fake addresses: CPU-only module")
 
 BASE = 0x7F0000000000

@@ -409,16 +409,16 @@ TWOSHOT_MODES = ["two", "fused", "linked"]
 
 
 def linked_workspace(B, n, k):
-    """A zero-filled workspace for pc_twoshot_linked (int32 words)."""
+    """A zero-filled workspace for pc_twoshot_linked (uint64 words)."""
     nbytes = B.pc_twoshot_linked_workspace_bytes(n, k)
     assert nbytes > 0
-    return torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device="cuda:0")
+    return torch.zeros((nbytes + 7) // 8, dtype=torch.int64, device="cuda:0")
 
 
 def check_linked_workspace(B, D, ws, calls):
     """After `calls` calls every workgroup's call counter reads `calls` and
     no wait was abandoned."""
-    w = D.down(ws, np.uint32)
+    w = D.down(ws, np.uint64)
     assert np.all(w[:B.PC_LINKED_GROUPS] == calls), np.unique(w[:B.PC_LINKED_GROUPS])
     assert w[B.PC_LINKED_STATUS_WORD] == 0
 
@@ -551,7 +551,7 @@ def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
     shapes = [(8, 8 * 65536), (3, 3 * 8 * 5000), (8, 8 * 65536), (8, 8 * 8 * 1024 * 70),
               (2, 16), (5, 5 * 8 * 256 * 3)]
     nbytes = max(B.pc_twoshot_linked_workspace_bytes(n, k) for n, k in shapes)
-    ws = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    ws = torch.zeros(nbytes // 8, dtype=torch.int64, device="cuda:0")
     for i, (n, k) in enumerate(shapes):
         say("linked reuse", i, n, k)
         xs = [synth.uniform_bf16(1500 + i, 0, r, k) for r in range(n)]

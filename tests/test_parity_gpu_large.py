@@ -160,7 +160,7 @@ def test_twoshot_forms_far(B, D, orc, size):
     g = gen(43)
     ins = [finite_bf16(k, g) for _ in range(n)]
     outs = [torch.empty(k, dtype=torch.int16, device=DEV) for _ in range(n)]
-    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8, dtype=torch.int64, device=DEV)
     spans = windows(k, byte_marks(k, 2) + [k // n], 8192, align=8)
     wants = [orc.reduce([D.down(x[a:b], np.uint16) for x in ins]) for a, b in spans]
     for form in ("pc_twoshot", "pc_twoshot_fused", "pc_twoshot_linked"):

@@ -83,7 +83,7 @@ def test_twoshot_properties(B, D, orc, data, n, form):
     elif form == "fused":
         B.pc_twoshot_fused(ins, outs, k)
     else:
-        ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 4, dtype=torch.int32, device="cuda:0")
+        ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8, dtype=torch.int64, device="cuda:0")
         B.pc_twoshot_linked(ins, outs, k, ws)
         assert int(ws[B.PC_LINKED_STATUS_WORD]) == 0
     want = orc.reduce(xs, threads=THREADS)
