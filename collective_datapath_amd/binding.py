@@ -26,14 +26,15 @@ PC_BLOCK_RECORD_BYTES = 136
 
 # Every symbol include/pc.h declares.
 EXPORTS = ("pc_copy", "pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes",
+           "pc_twoshot_linked", "pc_twoshot_linked_workspace_bytes", "pc_twoshot_linked_static",
            "pc_allgather_copy", "pc_publish_sentinel", "pc_consume_sentinel",
            "pc_reduce_validated", "pc_strerror", "pc_abi_version")
-PC_ABI_VERSION = 7          # the include/pc.h this binding is written against
+PC_ABI_VERSION = 8          # the include/pc.h this binding is written against
 PC_MAX_ATTEMPTS = 65536
 PC_LINKED_GROUPS = 256
 PC_LINKED_STATUS_WORD = 256       # uint64 words
 PC_LINKED_POLL_LIMIT_WORD = 257   # uint64 words
+PC_LINKED_STATIC_SCRATCH_BYTES = 1 << 20
 PC_SENTINEL = 0xFFFF
 
 if not os.path.exists(LIB_PATH):
@@ -74,12 +75,13 @@ _lib.pc_twoshot_fused.argtypes = [_P, _I, _P, _S, _P]
 _lib.pc_twoshot_linked.argtypes = [_P, _I, _P, _S, _P, _S, _P]
 _lib.pc_twoshot_linked_workspace_bytes.argtypes = [_I, _S]
 _lib.pc_twoshot_linked_workspace_bytes.restype = _S
+_lib.pc_twoshot_linked_static.argtypes = [_P, _I, _P, _S, _P, _P]
 _lib.pc_allgather_copy.argtypes = [_P, _I, _P, _S, ctypes.c_uint64, _P, _P]
 _lib.pc_publish_sentinel.argtypes = [_P, _P, _S, _P]
 _lib.pc_reduce_validated.argtypes = [_P, _P, _I, _P, _S, _S, ctypes.c_uint32, ctypes.c_uint32, _P, _P]
 _lib.pc_consume_sentinel.argtypes = [_P, _I, _P, _S, _P, _P]
 for _f in ("pc_copy", "pc_reduce", "pc_pack_ll", "pc_consume_ll", "pc_twoshot", "pc_twoshot_fused",
-           "pc_twoshot_linked", "pc_allgather_copy", "pc_publish_sentinel",
+           "pc_twoshot_linked", "pc_twoshot_linked_static", "pc_allgather_copy", "pc_publish_sentinel",
            "pc_consume_sentinel", "pc_reduce_validated"):
     getattr(_lib, _f).restype = _I
 _lib.pc_strerror.argtypes = [_I]
@@ -251,6 +253,19 @@ def pc_twoshot_linked(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int, 
                                 _addr(workspace, min(need, workspace_bytes), "workspace"),
                                 workspace_bytes, _stream(stream))
     return _call("pc_twoshot_linked", st, check)
+
+
+def pc_twoshot_linked_static(inputs: Sequence[Buffer], outs: Sequence[Buffer], k: int,
+                             gave_up: Optional[Buffer] = None, stream=None, check: bool = True) -> int:
+    """pc_twoshot_linked with the library's static workspace: allocates
+    nothing (include/pc.h, pc_twoshot_linked_static).  `gave_up`: optional
+    device word (int64 tensor) to which abandoned tiles are added."""
+    if len(outs) != len(inputs):
+        raise ValueError("pc_twoshot_linked_static needs one output per input")
+    st = _lib.pc_twoshot_linked_static(_addrs(inputs, 2 * k, "inputs"), len(inputs),
+                                       _addrs(outs, 2 * k, "outs"), k,
+                                       _addr(gave_up, 8, "gave_up"), _stream(stream))
+    return _call("pc_twoshot_linked_static", st, check)
 
 
 def pc_allgather_copy(shards: Sequence[Buffer], out: Buffer, shard_bytes: int, seq: int,

@@ -6,7 +6,8 @@
 // anything is launched (group size, 16-byte address and length alignment,
 // size ceiling), and a rejected call has no side effect.  Empty payloads are
 // legal no-ops so that every rank can issue the same call sequence
-// (Section 4.2).  Nothing here allocates or keeps state.
+// (Section 4.2).  Nothing here allocates; the only state is the per-device
+// address of the static workspace of pc_twoshot_linked_static.
 #include "../../include/pc.h"
 #include "pc_launch.hpp"
 
@@ -47,6 +48,8 @@ pc_status check_ptrs(const T* const* ptrs, int n) {
 inline pc_status from_hip(hipError_t e) { return e == hipSuccess ? PC_OK : PC_EHIP; }
 
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+inline bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 }  // namespace
 
@@ -189,6 +192,29 @@ pc_status pc_twoshot_linked(const uint16_t* const* inputs, int n, uint16_t* cons
         if (overlaps(workspace, need, inputs[r], bytes) || overlaps(workspace, need, outs[r], bytes))
             return PC_EINVAL;
     const hipError_t e = pcdp::launch_twoshot_linked(src, n, dst, k / 8 / (size_t)n, workspace, nullptr,
+                                                     static_cast<hipStream_t>(stream));
+    return e == hipErrorCooperativeLaunchTooLarge ? PC_EUNSUPPORTED : from_hip(e);
+}
+
+static_assert(PC_LINKED_STATIC_SCRATCH_BYTES == pcdp::kStaticScratchBytes, "static scratch size");
+
+pc_status pc_twoshot_linked_static(const uint16_t* const* inputs, int n, uint16_t* const* outs, size_t k,
+                                   uint64_t* gave_up, void* stream) {
+    const void* src[PC_MAX_RANKS];
+    void* dst[PC_MAX_RANKS];
+    bool empty;
+    if (pc_status st = check_twoshot(inputs, n, outs, k, src, dst, &empty)) return st;
+    if (empty) return PC_OK;
+    if (pc_twoshot_linked_workspace_bytes(n, k) > PC_LINKED_STATIC_SCRATCH_BYTES) return PC_EINVAL;
+    if (gave_up) {
+        if (!aligned8(gave_up)) return PC_EALIGN;
+        const size_t bytes = k * sizeof(uint16_t);
+        for (int r = 0; r < n; ++r)
+            if (overlaps(gave_up, 8, inputs[r], bytes) || overlaps(gave_up, 8, outs[r], bytes)) return PC_EINVAL;
+    }
+    void* ws = nullptr;
+    if (from_hip(pcdp::static_workspace(&ws))) return PC_EHIP;
+    const hipError_t e = pcdp::launch_twoshot_linked(src, n, dst, k / 8 / (size_t)n, ws, gave_up,
                                                      static_cast<hipStream_t>(stream));
     return e == hipErrorCooperativeLaunchTooLarge ? PC_EUNSUPPORTED : from_hip(e);
 }

@@ -46,6 +46,11 @@ size_t linked_tiles(int n, size_t nchunks_slice);
 hipError_t launch_twoshot_linked(const void* const* src, int n, void* const* outs,
                                  size_t nchunks_slice, void* workspace, void* status, hipStream_t stream);
 
+// The library's own workspace for the flag-linked twoshot, in static device
+// memory (kStaticScratchBytes per GPU): its address on the current device.
+constexpr size_t kStaticScratchBytes = (size_t)1 << 20;
+hipError_t static_workspace(void** ptr);
+
 // LL lines: 16-byte chunks of src -> 4 lines each.
 hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t seq,
                           hipStream_t stream);

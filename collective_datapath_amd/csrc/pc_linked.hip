@@ -248,6 +248,32 @@ static hipError_t go_linked_n(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint64_t* ws
     }
 }
 
+// ---- the same call with its workspace in static device memory --------------------
+// For callers that cannot allocate.  `scratch` is this library's workspace
+// of fixed size in every GPU's memory (zero when the code object is
+// loaded, as every static device variable); host code never uses the
+// array's name, only the per-device address hipGetSymbolAddress returns,
+// looked up on the first call on each device.  Calls on one device share
+// it, so calls that may overlap in time on one device race.
+__device__ __align__(256) uint64_t scratch[kStaticScratchBytes / sizeof(uint64_t)];
+
+hipError_t static_workspace(void** ptr) {
+    static std::atomic<void*> known[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = known[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        known[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 hipError_t launch_twoshot_linked(const void* const* src, int n, void* const* outs,
                                  size_t nchunks_slice, void* workspace, void* status, hipStream_t stream) {
     Ptrs<const u32x4*> s;

@@ -17,8 +17,9 @@
  *    arrays, read only during the call.  The pointers inside them and every
  *    other data pointer are DEVICE pointers on the current HIP device, each
  *    16-byte aligned.  The caller allocates and frees all memory; the library
- *    allocates nothing and keeps no state between calls (pc_twoshot_linked
- *    keeps its call counters in a workspace the caller owns).
+ *    allocates nothing and keeps no state between calls, apart from
+ *    pc_twoshot_linked_static's static workspace (pc_twoshot_linked keeps its
+ *    call counters in a workspace the caller owns).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously; outputs are valid once the stream has
  *    reached the call.  No call synchronizes the device.
@@ -74,7 +75,7 @@ enum {
     PC_EHIP = -4          /* the HIP runtime refused the launch              */
 };
 
-#define PC_ABI_VERSION 7
+#define PC_ABI_VERSION 8
 #define PC_MAX_RANKS 8
 #define PC_LL_LINE_BYTES 8          /* u32 data (element 2j low, 2j+1 high) | u32 seq   */
 #define PC_BLOCK_PAYLOAD_BYTES 128
@@ -244,6 +245,34 @@ PC_API size_t pc_twoshot_linked_workspace_bytes(int n, size_t k);
 PC_API pc_status pc_twoshot_linked(const uint16_t* const* inputs, int n, uint16_t* const* outs,
                                    size_t k, uint64_t* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * pc_twoshot_linked_static -- pc_twoshot_linked for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, result and status counting,
+ * with the workspace held by the library in static device memory instead of
+ * passed in.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller passes only inputs and outputs.
+ *   inputs, n, outs, k : as pc_twoshot_linked.  The workspace that
+ *            pc_twoshot_linked_workspace_bytes(n, k) would give must fit in
+ *            PC_LINKED_STATIC_SCRATCH_BYTES (1 MiB: about 2 GiB per rank at 8
+ *            ranks); larger calls are rejected with PC_EINVAL and nothing
+ *            is launched.
+ *   gave_up : device, 8-byte aligned, or NULL.  The number of tiles whose
+ *            wait was abandoned is added to *gave_up (NULL: to a word of the
+ *            static workspace that the caller cannot read).  It must not
+ *            overlap an input or output.
+ * The static workspace is zero when the library is loaded, lives until the
+ * process ends (one per GPU the library runs on) and keeps the call
+ * counters between calls, as a caller-owned workspace does.  Every call on
+ * one GPU shares it: calls that may overlap in time on one GPU (other
+ * streams) race and must not be issued.
+ * Errors: PC_EINVAL (also: the size limit above, gave_up overlapping a
+ * buffer), PC_EALIGN, PC_EUNSUPPORTED, PC_EHIP.
+ */
+#define PC_LINKED_STATIC_SCRATCH_BYTES ((size_t)1 << 20)
+PC_API pc_status pc_twoshot_linked_static(const uint16_t* const* inputs, int n, uint16_t* const* outs,
+                                          size_t k, uint64_t* gave_up, void* stream);
 
 /*
  * pc_allgather_copy -- gather N shards of sequence-stamped blocks.

@@ -269,3 +269,47 @@ def test_binding_rejects_host_and_short_tensors():
 def test_copy_validation(args, want):
     assert B.pc_copy(stream=0, check=False, **args) == want
 
+
+def static_limit(n):
+    """The largest k (a multiple of 8 * n) whose linked workspace fits in the
+    static scratch of pc_twoshot_linked_static."""
+    unit = 8 * n
+    lo, hi = unit, unit
+    while B.pc_twoshot_linked_workspace_bytes(n, hi) <= B.PC_LINKED_STATIC_SCRATCH_BYTES:
+        lo, hi = hi, 2 * hi
+    while hi - lo > unit:
+        mid = (lo + hi) // 2 // unit * unit
+        if B.pc_twoshot_linked_workspace_bytes(n, mid) <= B.PC_LINKED_STATIC_SCRATCH_BYTES:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_twoshot_linked_static_rejects_calls_beyond_its_scratch(n):
+    k = static_limit(n) + 8 * n
+    assert B.pc_twoshot_linked_workspace_bytes(n, k) > B.PC_LINKED_STATIC_SCRATCH_BYTES
+    # About 2 GiB per rank at 8 ranks: far-apart fake addresses, never touched.
+    big = 64 << 30
+    assert B.pc_twoshot_linked_static(ptrs(n, stride=big), ptrs(n, stride=big, base=A + 16 * big), k,
+                                      stream=0, check=False) == B.PC_EINVAL
+
+
+@pytest.mark.parametrize("gave_up,want", [
+    (A + 4096 * MB + 4, B.PC_EALIGN),          # not 8-byte aligned
+    (OUT + 8, B.PC_EINVAL),                    # inside outs[0]
+    (A + 8, B.PC_EINVAL),                      # inside inputs[0]
+])
+def test_twoshot_linked_static_gave_up_word_validation(gave_up, want):
+    n, k = 4, 4 * 8 * 300
+    assert B.pc_twoshot_linked_static(ptrs(n), ptrs(n, base=OUT), k, gave_up, stream=0,
+                                      check=False) == want
+
+
+def test_twoshot_linked_static_shares_twoshot_validation():
+    assert B.pc_twoshot_linked_static(ptrs(4), ptrs(4, base=OUT), 64 * 4 + 8, stream=0,
+                                      check=False) == B.PC_EALIGN
+    assert B.pc_twoshot_linked_static(ptrs(4), ptrs(4, base=A + 32), 64 * 4, stream=0,
+                                      check=False) == B.PC_EINVAL
+    assert B.pc_twoshot_linked_static([0] * 4, [0] * 4, 0, stream=0, check=False) == B.PC_OK
