@@ -1,10 +1,10 @@
 // pc_gather.hip -- all-gather copy of sequence-stamped 128-byte blocks.
 //
 // "flash-comm: Self-Synchronizing Collective Communication for LLM
-// Decoding", Section 4.3 (all-gather: each source publishes one shard and
-// receivers take each shard through the same readiness layer, with no
-// reduction) and Section 3.1 (a unit is accepted only when its sequence
-// number matches the current call); Appendix A, Table 8 discussion (128-byte
+// Decoding", Section 4.3 (the all-gather is the distribution half of the
+// all-reduce: shards pass through the same readiness check and are placed,
+// not folded) and Section 3.1 (sequence-number readiness: a stale number
+// means "not yet arrived"); Appendix A, Table 8 discussion (128-byte
 // writes were never observed torn).  "Purlin: Separating Orchestration from
 // the Datapath of Collectives", Section 3.1 (AllGather places the gathered
 // partitions in rank order).

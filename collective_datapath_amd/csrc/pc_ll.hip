@@ -2,9 +2,9 @@
 // validate-and-fold on the consumer side.
 //
 // "flash-comm: Self-Synchronizing Collective Communication for LLM
-// Decoding", Section 3.1 (sequence-number readiness: data and the call's
-// sequence number travel in one transfer unit; a receiver accepts the data
-// only when the number matches the current call), Section 4.3 (16-byte
+// Decoding", Section 3.1 (sequence-number readiness: payload and call number
+// share one store, so a line whose number is the current call's has fully
+// arrived and any other line is stale), Section 4.3 (16-byte
 // packet = 8 payload bytes + two copies of the sequence number; one-hop
 // reduce only after every source is ready, folded by source rank in rank
 // order) and Section 3.3 (fold order 0..N-1).  "Purlin: Separating
