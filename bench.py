@@ -45,6 +45,11 @@ TRAFFIC = {"bytes": 604666407,
                        "collective_datapath_amd/csrc/pc_device.hpp"),
            "sha256": "339bd0678691cbf41843069fcca8f4e82937559dea5756034dcb89d1c20b0360"}
 HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0>"
+# rocprofv3 kernel-trace statistics of the same kernel over >= 1,024
+# dispatches (profiles/k_reduce_staged_8x64MiB_trace.md), reported under the
+# same source-hash condition as TRAFFIC.
+KERNEL_TRACE = {"dispatches": 3405, "median_us": 89.869, "mean_us": 90.284,
+                "profile": "profiles/k_reduce_staged_8x64MiB_trace.md"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
 
@@ -778,6 +783,11 @@ def main():
             "config": {"workload": "oneshot reduce, N=8 ranks, K=4096x8192 bf16 (64 MiB/rank), "
                                    "normal(0,0.02), fp32 accumulate in rank order 0..7, bf16 RNE output",
                        "n": 8, "k": 4096 * 8192, "bytes_per_call": 9 * 2 * 4096 * 8192}}
+    if ach and "headline" in out and measured_traffic() is not None:
+        kt = dict(KERNEL_TRACE)
+        kt["gbs_at_median"] = round(gbs(out["headline"]["bytes_per_call"], kt["median_us"]), 1)
+        kt["frac_at_median"] = round(kt["gbs_at_median"] / HBM_PEAK_GBS, 4)
+        out["headline"]["rocprof_kernel_trace"] = kt
     if ach:
         line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
