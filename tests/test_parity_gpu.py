@@ -544,6 +544,30 @@ def test_bandwidth_regime_every_n(B, D, orc, n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n", [4, 5, 8])
+def test_staged_reduce_every_batch_remainder(B, D, orc, n):
+    """The LDS-staged persistent reduce (four or more ranks, working set of
+    64 MiB or more) takes a workgroup's tiles in batches of 8 and the rest
+    in batches of 4, 2 and 1.  3,839 tiles of 1,024 chunks (plus a ragged
+    tail) on 256 CUs give every workgroup 14 or 15 tiles: 8 + 4 + 2 and
+    8 + 4 + 2 + 1.  The oneshot runs it with a permuted order, twoshot
+    phase 1 with 3,839 tiles over n slices."""
+    chunks = 3838 * 1024 + 517
+    k = 8 * chunks
+    say("staged reduce remainders", n, k)
+    xs = [synth.uniform_bf16(1700 + n, 0, r, k) for r in range(n)]
+    order = list(np.random.default_rng(70 + n).permutation(n))
+    assert np.array_equal(gpu_reduce(B, D, xs, order=order),
+                          orc.reduce(xs, order=order, threads=THREADS))
+    sc = -(-3839 * 1024 // n) - 3                     # ragged slices, 128-byte grid
+    k2 = 8 * n * sc
+    xs2 = [synth.uniform_bf16(1710 + n, 0, r, k2) for r in range(n)]
+    want = orc.reduce(xs2, threads=THREADS)
+    for g in gpu_twoshot(B, D, xs2, "two"):
+        assert np.array_equal(g, want)
+    torch.cuda.empty_cache()
+
+
 def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
     """One workspace, many calls of different n and k (tile geometry changes
     between calls): the flags of earlier calls are never taken as ready, and
