@@ -974,8 +974,9 @@ def test_graph_replays_match_oracle(B, D, orc):
 def test_graph_replays_bandwidth_regime(B, D, orc):
     """Every large-size path captured once and replayed with new inputs from
     torch's device RNG written eagerly between replays: 8 ranks x 48 MiB takes
-    the two-launch, flag-linked and fused twoshots with their large shapes,
-    the persistent LL and speculative consumers, the two-pass sentinel
+    the staged oneshot reduce, the two-launch, flag-linked and fused twoshots
+    with their large shapes, the persistent LL and speculative consumers, the
+    two-pass sentinel
     consumer and the all-gather with non-temporal staging.  Outputs are
     checked at sampled positions against the oracle run on the sampled
     inputs; bitmaps, re-armed slots, attempts and the linked status word are
@@ -988,6 +989,7 @@ def test_graph_replays_bandwidth_regime(B, D, orc):
     ins = [torch.empty(k, dtype=torch.int16, device=dev) for _ in range(n)]
     outs = [torch.empty(k, dtype=torch.int16, device=dev) for _ in range(n)]
     louts = [torch.empty(k, dtype=torch.int16, device=dev) for _ in range(n)]
+    r_out = torch.empty(k, dtype=torch.int16, device=dev)
     ws = linked_workspace(B, n, k)
     lines = [torch.empty(nl, dtype=torch.int64, device=dev) for _ in range(n)]
     ll_out = torch.empty(k, dtype=torch.int16, device=dev)
@@ -1019,6 +1021,7 @@ def test_graph_replays_bandwidth_regime(B, D, orc):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
+            B.pc_reduce(ins, r_out, k)
             B.pc_twoshot(ins, outs, k)
             B.pc_twoshot_fused(ins, outs, k)
             B.pc_twoshot_linked(ins, louts, k, ws)
@@ -1045,7 +1048,7 @@ def test_graph_replays_bandwidth_regime(B, D, orc):
         say("bandwidth-regime graph replay", rep)
         xs = [D.down(t[idx], np.uint16) for t in ins]
         want = orc.reduce(xs)
-        for t in outs + louts + [ll_out, v_out]:
+        for t in outs + louts + [r_out, ll_out, v_out]:
             assert np.array_equal(D.down(t[idx], np.uint16), want), rep
         assert np.array_equal(D.down(s_out[idx], np.uint16),
                               orc.reduce([orc.publish_sentinel(x) for x in xs])), rep

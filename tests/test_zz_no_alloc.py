@@ -54,3 +54,15 @@ def test_static_workspace_matches_caller_workspace(B, D, orc):
             assert np.array_equal(g, want), (i, r)
         assert int(D.down(gave_up, np.uint64)[0]) == 0, i
         assert int(D.down(ws, np.uint64)[B.PC_LINKED_STATUS_WORD]) == 0, i
+
+
+def test_static_workspace_first_call_inside_a_capture(B):
+    """A fresh process whose first pc_twoshot_linked_static call is captured
+    in a graph: the static workspace's address is looked up during capture,
+    and every replay is exact."""
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "linked_static_capture_first.py")],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and "OK" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])
