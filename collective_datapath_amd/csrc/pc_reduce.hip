@@ -270,6 +270,10 @@ void k_twoshot_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nsl
             const __amdgpu_buffer_rsrc_t rd = tile_rsrc(dst.p[r] + at.first, (uint32_t)r == at.s ? 0u : at.bytes);
 #pragma unroll
             for (int u = 0; u < U; ++u) store16_rsrc<kPolicyNonTemporal>(rd, (u * kBlock + t) * 16u, v[u]);
+            // One output's stores at a time per wave: 168.3 vs 174.8 us at
+            // 8 ranks x 64 MiB (174 vs 196 on another MI355X), level at the
+            // other sizes and rank counts measured.
+            wait_vm<0>();
         }
     }
 }
@@ -299,6 +303,40 @@ __global__ __launch_bounds__(kBlock) void k_copyout(Ptrs<u32x4*> outs, uint32_t 
         const __amdgpu_buffer_rsrc_t rd = tile_rsrc(outs.p[r] + first, (uint32_t)r == s ? 0u : bytes);
 #pragma unroll
         for (int u = 0; u < U; ++u) store16_rsrc<kStorePolicy>(rd, (u * kBlock + t) * 16u, v[u]);
+    }
+}
+
+// ---- twoshot copy-out, one destination per workgroup (bandwidth regime) --------
+// Work item w copies one 4 KiB tile of one slice into one other output.  The
+// N-1 items of a tile get ids with the same remainder mod 8, and workgroups
+// are dispatched round-robin over the MI355X's 8 XCDs, so the N-1 copies of a
+// tile run on one XCD and all but the first read of it hit that XCD's L2.
+// HBM takes writes fastest from many short-lived workgroups that each write
+// a few KiB; k_copyout keeps up to (N-1) x 8 KiB of stores in flight per
+// workgroup.  At 8 ranks x 64 MiB, interleaved on one MI355X: 74.9 vs 85.8 us
+// for the copy-out, 168.9 vs 180.2 us for the whole call (the same work items
+// without the XCD grouping: 126.7 us).  From a grid cap of about 4M
+// workgroups a workgroup takes every grid-th item, keeping its remainder.
+constexpr uint32_t kXcds = 8;
+constexpr uint32_t kCopyDestGridCap = 1u << 22;
+constexpr int kCopyDestMinRanks = 7;
+
+template <int N>
+__global__ __launch_bounds__(kBlock) void k_copyout_dest(Ptrs<u32x4*> outs, uint32_t nslice,
+                                                         uint32_t tiles_per_slice, uint32_t items) {
+    const uint32_t ntiles = tiles_per_slice * N;
+    const uint32_t t = threadIdx.x;
+    for (uint32_t w = blockIdx.x; w < items; w += gridDim.x) {
+        const uint32_t rest = w / kXcds;
+        const uint32_t tile = rest / (N - 1) * kXcds + w % kXcds;
+        if (tile >= ntiles) continue;  // the last group of 8 tiles may be partial
+        const uint32_t di = rest % (N - 1);
+        const uint32_t s = tile / tiles_per_slice;
+        const uint32_t r = di < s ? di : di + 1;  // every output but the owner's
+        const SliceTile st = slice_tile(s, tile - s * tiles_per_slice, nslice, kBlock);
+        const uint32_t bytes = st.chunks * 16u;
+        const u32x4 v = load16_rsrc<0>(tile_rsrc(outs.p[s] + st.first, bytes), t * 16u);
+        store16_rsrc<kPolicyNonTemporal>(tile_rsrc(outs.p[r] + st.first, bytes), t * 16u, v);
     }
 }
 
@@ -417,12 +455,28 @@ static hipError_t dispatch_reduce(int n, Regime rg, Ptrs<const u32x4*> src, Ptrs
 // From 48 MiB per rank, where the two policies are level at 8 ranks, the
 // copies carry the non-temporal hint: 181 vs 192 us at 64 MiB per rank and
 // 269 vs 310 us at 96 MiB.  Below it the default policy is faster (87 vs
-// 92 us at 32 MiB), because the copies still find room in the caches.
+// 92 us at 32 MiB), because the copies still find room in the caches.  At
+// 7 and 8 ranks the copies then go one destination per workgroup
+// (k_copyout_dest); with fewer ranks that kernel measured level (4 to 6
+// ranks, within 1-3% either way at 64 and 96 MiB per rank) and is not used.
 constexpr size_t kCopyoutStreamBytes = (size_t)48 << 20;
+
+template <int N>
+static hipError_t go_copyout_dest(Ptrs<u32x4*> outs, uint32_t nslice, hipStream_t stream) {
+    uint32_t tiles_per_slice = slice_tiles(nslice, N, kBlock);
+    const uint32_t groups = (tiles_per_slice * N + kXcds - 1) / kXcds;
+    uint32_t items = groups * kXcds * (N - 1);
+    constexpr uint32_t kCap = kCopyDestGridCap / (kXcds * (N - 1)) * (kXcds * (N - 1));
+    const uint32_t grid = items < kCap ? items : kCap;  // a multiple of 8 either way
+    void* args[] = {&outs, &nslice, &tiles_per_slice, &items};
+    return hipLaunchKernel((const void*)&k_copyout_dest<N>, dim3(grid), dim3(kBlock), args, 0, stream);
+}
 
 template <int N>
 static hipError_t go_copyout(Ptrs<u32x4*> outs, uint32_t nslice, uint32_t slices, bool wide,
                              bool nt, hipStream_t stream) {
+    if constexpr (N >= kCopyDestMinRanks)
+        if (nt) return go_copyout_dest<N>(outs, nslice, stream);
     void* args[] = {&outs, &nslice};
     if (wide) {
         dim3 grid(slice_tiles(nslice, slices, 2 * kBlock), slices);

@@ -473,9 +473,11 @@ def test_twoshot_shapes(B, D, orc, n, slice_chunks, mode):
 
 
 # From 48 MiB per rank the copies of the two-launch and the flag-linked forms
-# carry the non-temporal hint; just below and past that size, with ragged
-# slices.
-@pytest.mark.parametrize("n,per_rank_mib,extra", [(8, 48, 3), (8, 47, 5), (2, 50, 1), (5, 64, 7)])
+# carry the non-temporal hint, and at 7 and 8 ranks the two-launch form's
+# copies go one destination per workgroup; just below and past that size,
+# with ragged slices.
+@pytest.mark.parametrize("n,per_rank_mib,extra", [(8, 48, 3), (8, 47, 5), (2, 50, 1), (5, 64, 7), (7, 49, 3),
+                                                  (7, 47, 1)])
 def test_twoshot_copies_nontemporal(B, D, orc, n, per_rank_mib, extra):
     sc = (per_rank_mib << 20) // (16 * n) + extra       # chunks per slice
     k = 8 * n * sc

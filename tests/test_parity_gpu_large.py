@@ -1,6 +1,7 @@
 """Byte offsets above 4 GiB, and the largest accepted size, for every entry
 point whose other tests stay below them (the reduce and the copy have their
-own).
+own); and one call large enough that a kernel's grid cap makes workgroups
+take several work items.
 
 Each call runs twice: on buffers that reach just past 2^32 bytes, with sizes
 ragged against every tile shape, and at the largest size it accepts
@@ -190,6 +191,26 @@ def test_twoshot_fused_split_past_4gib(B, D, orc):
     outs = [torch.full((k,), -1, dtype=torch.int16, device=DEV) for _ in range(n)]
     spans = windows(k, byte_marks(k, 2) + [s * k // n for s in range(1, n)], 8192, align=8)
     B.pc_twoshot_fused(ins, outs, k)
+    for a, b in spans:
+        want = orc.reduce([D.down(x[a:b], np.uint16) for x in ins])
+        for r, o in enumerate(outs):
+            assert np.array_equal(D.down(o[a:b], np.uint16), want), (r, a, b)
+
+
+def test_twoshot_copyout_past_its_grid_cap(B, D, orc):
+    # Eight ranks of 2.5 GiB + 896 B: the two-launch twoshot's copy-out, one
+    # destination per workgroup, has 8 x 81,921 tiles x 7 destinations =
+    # 4.59M work items, more than its grid of about 4.19M workgroups, so the
+    # first workgroups take a second item.
+    n = 8
+    k = ((5 * GiB // 4) // (8 * n) + 7) * 8 * n
+    need_memory(2 * n * 2 * k + 2 * GiB)
+    say("pc_twoshot copy-out past its grid cap", n, k)
+    g = gen(49)
+    ins = [finite_bf16(k, g) for _ in range(n)]
+    outs = [torch.full((k,), -1, dtype=torch.int16, device=DEV) for _ in range(n)]
+    spans = windows(k, byte_marks(k, 2) + [s * k // n for s in range(1, n)], 8192, align=8)
+    B.pc_twoshot(ins, outs, k)
     for a, b in spans:
         want = orc.reduce([D.down(x[a:b], np.uint16) for x in ins])
         for r, o in enumerate(outs):

@@ -6,8 +6,8 @@ outputs and still ends.  The test forces it from the host, with no kernel
 fault or hang: in a fresh zeroed workspace, workgroup 0's call counter is
 offset, so workgroup 0 stamps its flags with an epoch its consumer never
 waits for and waits for an epoch its producer never stamps; the poll limit
-word bounds each wait to a few polls.  (flash-comm, Section 4.4: bounded
-polling, then explicit verification.)
+word bounds each wait to a few thousand polls.  (flash-comm, Section 4.4:
+bounded polling, then explicit verification.)
 
 Stress: libpcdp_delay.so is the same library with the flag-linked twoshot
 built to sleep a pseudo-random time, different per workgroup, wave and
@@ -75,7 +75,11 @@ def test_twoshot_linked_gives_up_and_counts(B, D, orc):
     outs = [D.filled(k, 0xFFFF) for _ in range(n)]
     ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8, dtype=torch.int64, device=D.DEV)
     ws[0] = 5                                   # workgroup 0 runs five calls ahead
-    ws[B.PC_LINKED_POLL_LIMIT_WORD] = 64        # a wait gives up after 64 polls
+    # A wait gives up after 4,096 polls: milliseconds, so the planted waits
+    # end soon, while every producer that really runs publishes long before
+    # (64 polls, a few microseconds, also cut short waits for producers that
+    # merely started late).
+    ws[B.PC_LINKED_POLL_LIMIT_WORD] = 4096
     say("linked give-up", n, k)
     t0 = time.perf_counter()
     B.pc_twoshot_linked(ins, outs, k, ws)
