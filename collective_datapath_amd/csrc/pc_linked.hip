@@ -28,8 +28,10 @@
 //
 // Tile t = (slice s, tile j of the slice) covers up to 256*U chunks of 16
 // bytes of slice s.  Phase 1: workgroup t mod G folds tile t from the n
-// inputs into outs[s] (the owner's copy); once all of its tiles are stored
-// it publishes their flags behind one release at agent scope.  Phase 2:
+// inputs into outs[s] (the owner's copy), at 4 MiB per rank and above with
+// four or more ranks through the LDS stages of pc_staged.hpp; once all of
+// its tiles are stored it publishes their flags behind one release at agent
+// scope.  Phase 2:
 // workgroup (t + G/2) mod G waits for the flags of its tiles, acquires once
 // at agent scope, reads each owner tile and writes it to every other
 // outs[r].  Every workgroup finishes phase 1 before it waits on any flag,
@@ -53,6 +55,7 @@
 // natural schedule does not produce.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
+#include "pc_staged.hpp"
 
 #include <atomic>
 
@@ -78,7 +81,10 @@ __device__ __forceinline__ void stress_delay(uint64_t epoch, uint32_t who, uint3
 #endif
 }
 
-template <int N, int U, bool kStream, bool kNtCopies>
+// kStaged (tiles of 1024 chunks, four or more ranks): phase 1 runs the
+// LDS-staged fold of pc_staged.hpp, which fits this kernel's shape of one
+// 256-lane workgroup per CU.
+template <int N, int U, bool kStream, bool kNtCopies, bool kStaged>
 __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*> src,
                                                                 Ptrs<u32x4*> outs, uint64_t* ws,
                                                                 uint64_t* status,
@@ -107,23 +113,52 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
     // pattern of a grid-wide barrier).  Fences are few on purpose: each one
     // writes back or invalidates a whole L2 and they queue up per XCD.
     if (w < ntiles) {
-        for (size_t t = w; t < ntiles; t += kLinkGroups) {
-            const size_t s = t / tiles_per_slice;
-            const SliceTile st = slice_tile((uint32_t)s, (uint32_t)(t % tiles_per_slice), slice_chunks, kTile);
-            const size_t c0 = st.first;
-            const uint32_t bytes = st.chunks * 16u;
-            u32x4 v[U][N];
+        if constexpr (kStaged) {
+            static_assert(kTile == kStageTileChunks && N >= kStageMinRanks, "staged tile shape");
+            PC_STAGE_ARRAYS(N)
+            const uint32_t lane = tid & (kWave - 1), wave = tid / kWave;
+            for_each_stage_batch([&](auto tiles, uint32_t g0) {
+                constexpr int kTiles = decltype(tiles)::value;
+                StageTile tile[kTiles];
+                uint32_t slice[kTiles];
 #pragma unroll
-            for (int r = 0; r < N; ++r) {
-                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + c0, bytes);
+                for (int j = 0; j < kTiles; ++j) {
+                    const size_t t = g0 + (size_t)j * kLinkGroups;
+                    const size_t s = t / tiles_per_slice;
+                    const SliceTile st = slice_tile((uint32_t)s, (uint32_t)(t % tiles_per_slice), slice_chunks, kTile);
+                    tile[j] = {st.first, st.chunks * 16u};
+                    slice[j] = (uint32_t)s;
+                }
+                StagedBatch<N, false, kTiles> b{src, tile, {PC_STAGE_LIST}, wave, lane};
+                b.run();
+                __syncthreads();
+                stress_delay(epoch, w * 4 + wave, g0);
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[u][r] = load16_rsrc<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
+                for (int j = 0; j < 4 * kTiles; ++j) {
+                    const StageTile tl = tile[j / 4];
+                    store16_tile(tile_rsrc(outs.p[slice[j / 4]] + tl.first, tl.bytes), stage_row_offset(j, wave, lane),
+                                 b.res[j]);
+                }
+            }, (uint32_t)ntiles);
+        } else {
+            for (size_t t = w; t < ntiles; t += kLinkGroups) {
+                const size_t s = t / tiles_per_slice;
+                const SliceTile st = slice_tile((uint32_t)s, (uint32_t)(t % tiles_per_slice), slice_chunks, kTile);
+                const size_t c0 = st.first;
+                const uint32_t bytes = st.chunks * 16u;
+                u32x4 v[U][N];
+    #pragma unroll
+                for (int r = 0; r < N; ++r) {
+                    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + c0, bytes);
+    #pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[u][r] = load16_rsrc<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
+                }
+                stress_delay(epoch, w * 4 + tid / kWave, (uint32_t)t);
+                const __amdgpu_buffer_rsrc_t ro = tile_rsrc(outs.p[s] + c0, bytes);
+    #pragma unroll
+                for (int u = 0; u < U; ++u) store16_tile(ro, (u * kLinkBlock + tid) * 16u, fold_chunk<N>(v[u]));
             }
-            stress_delay(epoch, w * 4 + tid / kWave, (uint32_t)t);
-            const __amdgpu_buffer_rsrc_t ro = tile_rsrc(outs.p[s] + c0, bytes);
-#pragma unroll
-            for (int u = 0; u < U; ++u) store16_tile(ro, (u * kLinkBlock + tid) * 16u, fold_chunk<N>(v[u]));
         }
         __syncthreads();
         if (tid == 0) {
@@ -212,20 +247,50 @@ static hipError_t resident_capacity(const void* kernel, int* capacity) {
     return hipSuccess;
 }
 
-template <int N, int U, bool kStream, bool kNtCopies>
-static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint64_t* ws, uint64_t* status,
-                            size_t slice_chunks, hipStream_t stream) {
-    const void* kernel = (const void*)&k_twoshot_linked<N, U, kStream, kNtCopies>;
+// Workgroups of kernel K that fit on the current device at once, looked up
+// once per device.
+template <const void* (*K)()>
+static hipError_t cached_capacity(int* cap) {
     // 0 = not yet known, else capacity + 1, per device.
     static std::atomic<int> known[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int cap = dev >= 0 && dev < 64 ? known[dev].load(std::memory_order_relaxed) - 1 : -1;
-    if (cap < 0) {
-        e = resident_capacity(kernel, &cap);
+    *cap = dev >= 0 && dev < 64 ? known[dev].load(std::memory_order_relaxed) - 1 : -1;
+    if (*cap < 0) {
+        e = resident_capacity(K(), cap);
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) known[dev].store(cap + 1, std::memory_order_relaxed);
+        if (dev >= 0 && dev < 64) known[dev].store(*cap + 1, std::memory_order_relaxed);
+    }
+    return hipSuccess;
+}
+
+template <int N, int U, bool kStream, bool kNtCopies, bool kStaged>
+const void* linked_kernel() {
+    return (const void*)&k_twoshot_linked<N, U, kStream, kNtCopies, kStaged>;
+}
+
+// The staged phase 1 takes over half of a CU's LDS, so only one workgroup of
+// it fits per CU: it is launched where the whole grid still fits at once
+// (every MI355X CU in one partition), else the kernel that loads into
+// registers is.  At 8 ranks, interleaved on one MI355X: 187.9 vs 192.7 us at
+// 64 MiB per rank, 144.1 vs 147.2 at 48, 275.8 vs 286.8 at 96; 4 ranks
+// 99.2 vs 103.1 at 64 MiB and 29.0 vs 29.9 at 16.
+template <int N, int U, bool kStream, bool kNtCopies>
+static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint64_t* ws, uint64_t* status,
+                            size_t slice_chunks, hipStream_t stream) {
+    constexpr bool kCanStage = kStream && U * kLinkBlock == (int)kStageTileChunks && N >= kStageMinRanks;
+    int cap = 0;
+    const void* kernel = linked_kernel<N, U, kStream, kNtCopies, false>();
+    hipError_t e;
+    if constexpr (kCanStage) {
+        e = cached_capacity<linked_kernel<N, U, kStream, kNtCopies, true>>(&cap);
+        if (e != hipSuccess) return e;
+        if (cap >= (int)kLinkGroups) kernel = linked_kernel<N, U, kStream, kNtCopies, true>();
+    }
+    if (cap < (int)kLinkGroups) {
+        e = cached_capacity<linked_kernel<N, U, kStream, kNtCopies, false>>(&cap);
+        if (e != hipSuccess) return e;
     }
     if (cap < (int)kLinkGroups) return hipErrorCooperativeLaunchTooLarge;
     size_t tiles_per_slice = slice_tiles(slice_chunks, N, kLinkBlock * U);

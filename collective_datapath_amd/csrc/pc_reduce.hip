@@ -409,7 +409,6 @@ static hipError_t go_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
 // Whole rounds of one workgroup per CU, then as few workgroups as give that
 // many rounds, so every workgroup does the same number of tiles (to within
 // one).  The dynamic LDS request keeps a second workgroup off each CU.
-constexpr int kStagedMinRanks = 4;
 template <int N, Out kOut>
 static hipError_t go_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                                    uint32_t slices, hipStream_t stream) {
@@ -428,7 +427,7 @@ static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4
                                    uint32_t nslice, uint32_t slices, hipStream_t stream) {
     switch (rg) {
         case Regime::kStream:
-            if constexpr (kOut == Out::kAll || N < kStagedMinRanks)
+            if constexpr (kOut == Out::kAll || N < kStageMinRanks)
                 return go_reduce_persistent<N, kOut>(src, dst, nslice, slices, stream);
             else return go_reduce_staged<N, kOut>(src, dst, nslice, slices, stream);
         case Regime::kMid: return go_reduce<N, 2, false, kOut>(src, dst, nslice, slices, stream);

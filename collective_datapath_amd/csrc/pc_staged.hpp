@@ -48,6 +48,11 @@ constexpr uint32_t kStageTileChunks = 1024;          // chunks per tile per rank
 constexpr uint32_t kStageBlock = 256;                // lanes per workgroup
 constexpr uint32_t kStageMinLdsBytes = 84u << 10;    // over half of the CU's LDS
 constexpr int kStageMaxDepth = 8;
+// Ranks from which the staged folds are used: with 2 ranks the staged
+// reduce lost to the register kernel (29.4 vs 28.5 us at 8 ranks' worth of
+// bytes), and below 4 ranks a workgroup's stages no longer fill over half of
+// the CU's LDS.
+constexpr int kStageMinRanks = 4;
 
 // Stages per wave: about 24 KiB of a wave's loads in flight, at least 3
 // stages, at most 8 (the number of stage arrays).
