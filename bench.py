@@ -39,16 +39,16 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_staged_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604651048,
+TRAFFIC = {"bytes": 604593402,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_staged.hpp",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "e0658e89e007a17f9d0aeb3f1e8e09a78b684260f86f4bba8216d18869a41ba8"}
-HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0>"
+           "sha256": "f13730425c0ec5baa5544f3d5e235f1447961776c63bebbd367138e2c45c60c4"}
+HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0, true>"
 # rocprofv3 kernel-trace statistics of the same kernel over >= 1,024
 # dispatches (profiles/k_reduce_staged_8x64MiB_trace.md), reported under the
 # same source-hash condition as TRAFFIC.
-KERNEL_TRACE = {"dispatches": 3405, "median_us": 93.268, "mean_us": 93.494,
+KERNEL_TRACE = {"dispatches": 3405, "median_us": 92.669, "mean_us": 92.885,
                 "profile": "profiles/k_reduce_staged_8x64MiB_trace.md"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 

@@ -570,6 +570,28 @@ def test_staged_reduce_every_batch_remainder(B, D, orc, n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n", [4, 5, 8])
+def test_staged_reduce_whole_tiles(B, D, orc, n):
+    """Slices that are whole numbers of 1,024-chunk tiles take the staged
+    kernel built with a constant tile size: 3,840 whole tiles on 256 CUs,
+    15 per workgroup (8 + 4 + 2 + 1), for the oneshot (permuted order) and
+    for twoshot phase 1 with slices of whole tiles."""
+    chunks = 3840 * 1024
+    k = 8 * chunks
+    say("staged reduce whole tiles", n, k)
+    xs = [synth.uniform_bf16(1800 + n, 0, r, k) for r in range(n)]
+    order = list(np.random.default_rng(80 + n).permutation(n))
+    assert np.array_equal(gpu_reduce(B, D, xs, order=order),
+                          orc.reduce(xs, order=order, threads=THREADS))
+    sc = 1024 * -(-3840 // n)                           # whole tiles per slice
+    k2 = 8 * n * sc
+    xs2 = [synth.uniform_bf16(1810 + n, 0, r, k2) for r in range(n)]
+    want = orc.reduce(xs2, threads=THREADS)
+    for g in gpu_twoshot(B, D, xs2, "two"):
+        assert np.array_equal(g, want)
+    torch.cuda.empty_cache()
+
+
 def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
     """One workspace, many calls of different n and k (tile geometry changes
     between calls): the flags of earlier calls are never taken as ready, and
@@ -739,14 +761,7 @@ def test_consume_sentinel_shapes(B, D, orc, n, k):
     assert all(np.array_equal(g, w) for g, w in zip(got_slots, want_slots))
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_consume_sentinel_bandwidth_regime(B, D, orc, n):
-    # From 768 MiB of slots read plus results and re-arms written the call
-    # runs as a persistent fold and a separate re-arm pass.  Three 512-element
-    # units past that size leave ragged last blocks; ranks 0, 3 and 6 have
-    # about 2% of their packs missing and 1% torn (upper half unwritten).
-    k = (-(-(768 << 20) // (2 * (2 * n + 1))) // 512 + 3) * 512
-    say("consume_sentinel bandwidth regime", n, k)
+def consume_sentinel_bandwidth_regime(B, D, orc, n, k):
     pick = np.random.default_rng(900 + n)
     slots = []
     for r in range(n):
@@ -762,6 +777,26 @@ def test_consume_sentinel_bandwidth_regime(B, D, orc, n):
     assert all(np.array_equal(g, w) for g, w in zip(got_slots, want_slots))
     del slots, got_slots, want_slots
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_consume_sentinel_bandwidth_regime(B, D, orc, n):
+    # From 768 MiB of slots read plus results and re-arms written the call
+    # runs as a persistent fold and a separate re-arm pass.  Three 512-element
+    # units past that size leave ragged last blocks; ranks 0, 3 and 6 have
+    # about 2% of their packs missing and 1% torn (upper half unwritten).
+    k = (-(-(768 << 20) // (2 * (2 * n + 1))) // 512 + 3) * 512
+    say("consume_sentinel bandwidth regime", n, k)
+    consume_sentinel_bandwidth_regime(B, D, orc, n, k)
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_consume_sentinel_bandwidth_regime_whole_tiles(B, D, orc, n):
+    # The same past the switch with k a multiple of 8,192 elements: every
+    # 1,024-pack tile of the fold is whole, with no ragged last tile.
+    k = -(-(768 << 20) // (2 * (2 * n + 1) * 8192)) * 8192
+    say("consume_sentinel bandwidth regime, whole tiles", n, k)
+    consume_sentinel_bandwidth_regime(B, D, orc, n, k)
 
 
 def test_consume_sentinel_late_arrival(B, D, orc):
