@@ -43,7 +43,7 @@ TRAFFIC = {"bytes": 604593402,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_staged.hpp",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "f13730425c0ec5baa5544f3d5e235f1447961776c63bebbd367138e2c45c60c4"}
+           "sha256": "5dfc677ad3eddf29939562eb462e3b613694977891680d4e0109af31552c470b"}
 HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0, true>"
 # rocprofv3 kernel-trace statistics of the same kernel over >= 1,024
 # dispatches (profiles/k_reduce_staged_8x64MiB_trace.md), reported under the

@@ -23,7 +23,9 @@
 // (k_reduce_persistent).  Three output modes cover the oneshot reduce,
 // twoshot phase 1 and the single-launch twoshot; at the largest sizes the
 // single-launch twoshot folds first and hands its tiles out afterwards, in
-// the same launch (k_twoshot_persistent).
+// the same launch (k_twoshot_persistent).  The two-launch twoshot's second
+// kernel copies each owner slice out (k_copyout), at 7 and 8 ranks from
+// 48 MiB per rank with one destination per workgroup (k_copyout_dest).
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 #include "pc_staged.hpp"
