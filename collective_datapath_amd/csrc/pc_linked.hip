@@ -147,16 +147,16 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
                 const size_t c0 = st.first;
                 const uint32_t bytes = st.chunks * 16u;
                 u32x4 v[U][N];
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < N; ++r) {
                     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + c0, bytes);
-    #pragma unroll
+#pragma unroll
                     for (int u = 0; u < U; ++u)
                         v[u][r] = load16_rsrc<kLoadPolicy>(rs, (u * kLinkBlock + tid) * 16u);
                 }
                 stress_delay(epoch, w * 4 + tid / kWave, (uint32_t)t);
                 const __amdgpu_buffer_rsrc_t ro = tile_rsrc(outs.p[s] + c0, bytes);
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < U; ++u) store16_tile(ro, (u * kLinkBlock + tid) * 16u, fold_chunk<N>(v[u]));
             }
         }
@@ -266,7 +266,7 @@ static hipError_t cached_capacity(int* cap) {
 }
 
 template <int N, int U, bool kStream, bool kNtCopies, bool kStaged>
-const void* linked_kernel() {
+static const void* linked_kernel() {
     return (const void*)&k_twoshot_linked<N, U, kStream, kNtCopies, kStaged>;
 }
 
