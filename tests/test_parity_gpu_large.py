@@ -197,6 +197,58 @@ def test_twoshot_fused_split_past_4gib(B, D, orc):
             assert np.array_equal(D.down(o[a:b], np.uint16), want), (r, a, b)
 
 
+@pytest.mark.parametrize("shape", ["ragged", "whole_tiles"])
+def test_staged_paths_past_4gib(B, D, orc, shape):
+    # Four ranks of 4 GiB + 64 KiB (slices of whole 1,024-chunk tiles) or of
+    # 4 GiB + 32,896 B (ragged): the LDS-staged oneshot, twoshot phase 1 and
+    # the flag-linked twoshot's staged phase 1, each past byte offset 2^32.
+    n = 4
+    k = FAR // 2 + (32768 if shape == "whole_tiles" else 8 * n * 514)
+    need_memory(3 * n * 2 * k + 2 * GiB)
+    say("staged paths past 4 GiB", shape, n, k)
+    g = gen(52)
+    ins = [finite_bf16(k, g) for _ in range(n)]
+    outs = [torch.full((k,), -1, dtype=torch.int16, device=DEV) for _ in range(n)]
+    spans = windows(k, byte_marks(k, 2) + [s * k // n for s in range(1, n)], 8192, align=8)
+    wants = [orc.reduce([D.down(x[a:b], np.uint16) for x in ins]) for a, b in spans]
+    B.pc_reduce(ins, outs[0], k)
+    for (a, b), want in zip(spans, wants):
+        assert np.array_equal(D.down(outs[0][a:b], np.uint16), want), ("reduce", a, b)
+    ws = torch.zeros(B.pc_twoshot_linked_workspace_bytes(n, k) // 8, dtype=torch.int64, device=DEV)
+    for form in ("pc_twoshot", "pc_twoshot_linked"):
+        for o in outs:
+            o.fill_(-1)
+        if form == "pc_twoshot_linked":
+            B.pc_twoshot_linked(ins, outs, k, ws)
+        else:
+            B.pc_twoshot(ins, outs, k)
+        for (a, b), want in zip(spans, wants):
+            for r, o in enumerate(outs):
+                assert np.array_equal(D.down(o[a:b], np.uint16), want), (form, r, a, b)
+    torch.cuda.synchronize()
+    assert int(ws[B.PC_LINKED_STATUS_WORD]) == 0
+
+
+def test_twoshot_copyout_one_destination_past_4gib(B, D, orc):
+    # Seven ranks of 4 GiB + 3,552 B: the two-launch twoshot's copy-out with
+    # one destination per workgroup, past byte offset 2^32 and past its grid
+    # cap (about 1.05M tiles x 6 destinations = 6.3M work items, against a
+    # grid of about 4.19M workgroups).
+    n = 7
+    k = (FAR // 2 // (8 * n) + 32) * 8 * n
+    need_memory(2 * n * 2 * k + 2 * GiB)
+    say("twoshot one-destination copy-out past 4 GiB", n, k)
+    g = gen(53)
+    ins = [finite_bf16(k, g) for _ in range(n)]
+    outs = [torch.full((k,), -1, dtype=torch.int16, device=DEV) for _ in range(n)]
+    spans = windows(k, byte_marks(k, 2) + [s * k // n for s in range(1, n)], 8192, align=8)
+    B.pc_twoshot(ins, outs, k)
+    for a, b in spans:
+        want = orc.reduce([D.down(x[a:b], np.uint16) for x in ins])
+        for r, o in enumerate(outs):
+            assert np.array_equal(D.down(o[a:b], np.uint16), want), (r, a, b)
+
+
 def test_twoshot_copyout_past_its_grid_cap(B, D, orc):
     # Eight ranks of 2.5 GiB + 896 B: the two-launch twoshot's copy-out, one
     # destination per workgroup, has 8 x 81,921 tiles x 7 destinations =
