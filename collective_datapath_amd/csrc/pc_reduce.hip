@@ -205,8 +205,10 @@ void k_reduce_persistent(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nsli
 // of the tile), so the tile size is a constant rather than a value per tile,
 // and fewer scalar registers stay live across a batch (with a size per tile
 // they spill to VGPR lanes).  At 8 ranks x 64 MiB, interleaved on one
-// MI355X: 87.9 vs 89.5 us (91.7 vs 92.9 on a slower box).
-template <int N, Out kOut, bool kWhole>
+// MI355X: 87.9 vs 89.5 us (91.7 vs 92.9 on a slower box).  kDiagonal: the
+// ranks' loads run on a diagonal (DiagonalBatch in pc_staged.hpp), chosen
+// by bases_congruent from the rank buffers' addresses.
+template <int N, Out kOut, bool kWhole, bool kDiagonal>
 __global__ __launch_bounds__(kStageBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                      uint32_t tiles_per_slice, uint32_t ntiles) {
@@ -223,7 +225,8 @@ void k_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
             tile[j] = {at.first, kWhole ? kStageTileChunks * 16u : at.bytes};
             slice[j] = at.s;
         }
-        StagedBatch<N, false, kTiles> b{src, tile, {PC_STAGE_LIST}, w, lane};
+        std::conditional_t<kDiagonal, DiagonalBatch<N, kTiles>, StagedBatch<N, false, kTiles>> b{
+            src, tile, {PC_STAGE_LIST}, w, lane};
         b.run();
         __syncthreads();
 #pragma unroll
@@ -427,8 +430,12 @@ static hipError_t go_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uin
     void* args[] = {&src, &dst, &nslice, &tiles_per_slice, &ntiles};
     // Slices that are whole numbers of tiles start on the 128-byte grid, so
     // every tile of every slice is whole.
-    const void* k = nslice % kStageTileChunks == 0 ? (const void*)&k_reduce_staged<N, kOut, true>
-                                                   : (const void*)&k_reduce_staged<N, kOut, false>;
+    const bool whole = nslice % kStageTileChunks == 0;
+    const bool diagonal = bases_congruent((const void* const*)src.p, N);
+    const void* k = whole ? (diagonal ? (const void*)&k_reduce_staged<N, kOut, true, true>
+                                      : (const void*)&k_reduce_staged<N, kOut, true, false>)
+                          : (diagonal ? (const void*)&k_reduce_staged<N, kOut, false, true>
+                                      : (const void*)&k_reduce_staged<N, kOut, false, false>);
     return hipLaunchKernel(k, dim3(grid), dim3(kStageBlock), args, stage_pad_bytes<N>(), stream);
 }
 

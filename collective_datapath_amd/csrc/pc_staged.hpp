@@ -185,6 +185,130 @@ struct StagedBatch {
 // batches of 4, 2 and 1.  The body is a generic lambda of the kernel, so it
 // names the kernel's stage arrays directly (held behind a pointer table the
 // compiler lost track of them and spilled).
+// The same batch with the ranks on a diagonal: at step t, rank r loads row
+// t - r, so at any moment the ranks' loads sit one row (4 KiB) apart instead
+// of at the same offset of every rank buffer.  Rank buffers whose bases are
+// congruent modulo 32 KiB put same-offset loads into the same DRAM banks on
+// different pages.  The 8 x 64 MiB reduce took 92.4 - 93.5 us on such
+// layouts (separate allocations, which agree modulo 2 MiB: 88.2 - 92.3 us,
+// depending on where they landed) against 86.6 - 87.3 us with the rank
+// buffers 4 to 16 KiB apart; on the diagonal the congruent layouts took
+// 87.0 - 88.8 us.  bases_congruent below chooses it.  Row j is still folded
+// in rank order 0..N-1: its accumulators take rank r at step j + r.  Each
+// step reads one stage of N rows (one per rank) as before; a batch takes
+// 4 * kTiles + N - 1 steps, the first and last N - 1 with fewer loads.
+template <int N, int kTiles>
+struct DiagonalBatch {
+    static constexpr int S = stage_depth<N>();
+    static constexpr int kRows = 4 * kTiles;
+    static constexpr int kSteps = kRows + N - 1;
+    const Ptrs<const u32x4*>& src;
+    const StageTile (&tile)[kTiles];
+    u32x4* const stage[kStageMaxDepth];
+    const uint32_t w, lane;
+    u32x4 res[kRows];
+    float acc[kRows][8];
+
+    // Ranks that load at step t: rows t - r within [0, kRows).
+    static constexpr int first_rank(int t) { return t - (kRows - 1) > 0 ? t - (kRows - 1) : 0; }
+    static constexpr int last_rank(int t) { return t < N - 1 ? t : N - 1; }
+    static constexpr int loads_at(int t) { return t < 0 || t >= kSteps ? 0 : last_rank(t) - first_rank(t) + 1; }
+    // Loads issued after step t's own when step t waits: those of steps
+    // t + 1 .. t + S - 1.
+    static constexpr int loads_after(int t) {
+        int n = 0;
+        for (int u = t + 1; u < t + S && u < kSteps; ++u) n += loads_at(u);
+        return n;
+    }
+
+    template <int T, int R>
+    __device__ __forceinline__ void issue_rank() {
+        if constexpr (R >= first_rank(T) && R <= last_rank(T)) {
+            constexpr int J = T - R;
+            const StageTile t = tile[J / 4];
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[R] + t.first, t.bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage[T % S] + (w * N + R) * 64), 16,
+                                                     ((J % 4) * 256 + w * 64 + lane) * 16u, 0, 0,
+                                                     kPolicyNonTemporal);
+        }
+    }
+
+    template <int T, int... Rs>
+    __device__ __forceinline__ void issue(std::integer_sequence<int, Rs...>) {
+        (issue_rank<T, Rs>(), ...);
+    }
+
+    template <int T>
+    __device__ __forceinline__ void issue() {
+        if constexpr (T < kSteps) issue<T>(std::make_integer_sequence<int, N>{});
+    }
+
+    template <int T, int R>
+    __device__ __forceinline__ void fold_rank(const u32x4* st) {
+        if constexpr (R >= first_rank(T) && R <= last_rank(T)) {
+            constexpr int J = T - R;
+            const u32x4 v = st[(w * N + R) * 64 + lane];
+            if constexpr (R == 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[J][e] = -0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[J][2 * e] = acc[J][2 * e] + widen_lo(v[e]);
+                acc[J][2 * e + 1] = acc[J][2 * e + 1] + widen_hi(v[e]);
+            }
+            if constexpr (R == N - 1) {
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = narrow_pair(acc[J][2 * e], acc[J][2 * e + 1]);
+                res[J] = o;
+            }
+        }
+    }
+
+    template <int T, int... Rs>
+    __device__ __forceinline__ void fold(const u32x4* st, std::integer_sequence<int, Rs...>) {
+        (fold_rank<T, Rs>(st), ...);
+    }
+
+    template <int T>
+    __device__ __forceinline__ void prime() {
+        if constexpr (T < S) issue<T>();
+    }
+
+    template <int T>
+    __device__ __forceinline__ void step() {
+        wait_vm<loads_after(T)>();
+        fold<T>(stage[T % S], std::make_integer_sequence<int, N>{});
+        if constexpr (T + S < kSteps) {
+            wait_lds_reads();  // the stage is refilled only after it has been read
+            issue<T + S>();
+        }
+    }
+
+    template <int... Ts>
+    __device__ __forceinline__ void run(std::integer_sequence<int, Ts...>) {
+        (prime<Ts>(), ...);
+        (step<Ts>(), ...);
+    }
+
+    __device__ __forceinline__ void run() { run(std::make_integer_sequence<int, kSteps>{}); }
+};
+
+// Which batch a launch takes: the diagonal when every rank buffer's base is
+// congruent to rank 0's modulo kBankPeriod.  Measured on the 8 x 64 MiB
+// reduce with the rank buffers 0, 32 KiB, 64 KiB, 128 KiB, 1 MiB or 2 MiB
+// apart (and in separate allocations) the diagonal was faster or level;
+// with the buffers 4 to 16 KiB apart the plain pipeline already ran at
+// 86.6 - 87.3 us, and the diagonal would cancel a 4 KiB spacing.
+constexpr uintptr_t kBankPeriod = 32u << 10;
+
+__host__ inline bool bases_congruent(const void* const* p, int n) {
+    for (int r = 1; r < n; ++r)
+        if (((uintptr_t)p[r] - (uintptr_t)p[0]) % kBankPeriod != 0) return false;
+    return true;
+}
+
 template <typename Body>
 __device__ __forceinline__ void for_each_stage_batch(const Body& body, uint32_t ntiles) {
     const uint32_t stride = gridDim.x;

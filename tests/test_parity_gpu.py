@@ -592,6 +592,44 @@ def test_staged_reduce_whole_tiles(B, D, orc, n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n", [4, 7, 8])
+@pytest.mark.parametrize("shape", ["whole", "ragged"])
+@pytest.mark.parametrize("layout", ["congruent", "skewed"])
+def test_staged_reduce_rank_layouts(B, D, orc, n, shape, layout):
+    """The staged kernels take the ranks on a diagonal when every rank
+    buffer's base agrees with rank 0's modulo 32 KiB, and the plain pipeline
+    otherwise.  The rank buffers are carved from one allocation at a stride
+    that is a multiple of 32 KiB (congruent) or 4 KiB more (skewed), with
+    whole 1,024-chunk tiles or a ragged tail, for the oneshot (permuted order)
+    and twoshot phase 1."""
+    if shape == "whole":
+        chunks = n * 1024 * -(-3840 // n)              # whole tiles, also per twoshot slice
+    else:
+        chunks = 3838 * 1024 + 517
+        chunks -= chunks % n                           # twoshot slices: k a multiple of 8 n
+    k = 8 * chunks
+    stride = -(-2 * k // 32768) * 32768 // 2 + (2048 if layout == "skewed" else 0)   # elements
+    say("staged reduce layouts", n, k, shape, layout)
+    base = torch.empty(stride * n, dtype=torch.int16, device="cuda:0")
+    views = [base[r * stride:r * stride + k] for r in range(n)]
+    congruent = all((v.data_ptr() - views[0].data_ptr()) % 32768 == 0 for v in views)
+    assert congruent == (layout == "congruent")
+    xs = [synth.uniform_bf16(1900 + n, 0, r, k) for r in range(n)]
+    for v, x in zip(views, xs):
+        v.copy_(torch.from_numpy(x.view(np.int16)).to("cuda:0"))
+    order = list(np.random.default_rng(90 + n).permutation(n))
+    out = D.filled(k, 0xFFFF)
+    B.pc_reduce(views, out, k, order=order)
+    assert np.array_equal(D.down(out, np.uint16), orc.reduce(xs, order=order, threads=THREADS))
+    want = orc.reduce(xs, threads=THREADS)
+    outs = [D.filled(k, 0xFFFF) for _ in range(n)]
+    B.pc_twoshot(views, outs, k)
+    for o in outs:
+        assert np.array_equal(D.down(o, np.uint16), want)
+    del base, views, outs
+    torch.cuda.empty_cache()
+
+
 def test_twoshot_linked_reuses_workspace_across_sizes(B, D, orc):
     """One workspace, many calls of different n and k (tile geometry changes
     between calls): the flags of earlier calls are never taken as ready, and
