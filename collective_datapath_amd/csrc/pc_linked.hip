@@ -83,8 +83,9 @@ __device__ __forceinline__ void stress_delay(uint64_t epoch, uint32_t who, uint3
 
 // kStaged (tiles of 1024 chunks, four or more ranks): phase 1 runs the
 // LDS-staged fold of pc_staged.hpp, which fits this kernel's shape of one
-// 256-lane workgroup per CU.
-template <int N, int U, bool kStream, bool kNtCopies, bool kStaged>
+// 256-lane workgroup per CU; kDiagonal: with the ranks on a diagonal
+// (rank buffers whose bases agree modulo 32 KiB, as for the reduce).
+template <int N, int U, bool kStream, bool kNtCopies, bool kStaged, bool kDiagonal = false>
 __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*> src,
                                                                 Ptrs<u32x4*> outs, uint64_t* ws,
                                                                 uint64_t* status,
@@ -129,7 +130,8 @@ __global__ __launch_bounds__(kLinkBlock) void k_twoshot_linked(Ptrs<const u32x4*
                     tile[j] = {st.first, st.chunks * 16u};
                     slice[j] = (uint32_t)s;
                 }
-                StagedBatch<N, false, kTiles> b{src, tile, {PC_STAGE_LIST}, wave, lane};
+                std::conditional_t<kDiagonal, DiagonalBatch<N, kTiles>, StagedBatch<N, false, kTiles>> b{
+                    src, tile, {PC_STAGE_LIST}, wave, lane};
                 b.run();
                 __syncthreads();
                 stress_delay(epoch, w * 4 + wave, g0);
@@ -265,9 +267,9 @@ static hipError_t cached_capacity(int* cap) {
     return hipSuccess;
 }
 
-template <int N, int U, bool kStream, bool kNtCopies, bool kStaged>
+template <int N, int U, bool kStream, bool kNtCopies, bool kStaged, bool kDiagonal = false>
 static const void* linked_kernel() {
-    return (const void*)&k_twoshot_linked<N, U, kStream, kNtCopies, kStaged>;
+    return (const void*)&k_twoshot_linked<N, U, kStream, kNtCopies, kStaged, kDiagonal>;
 }
 
 // The staged phase 1 takes over half of a CU's LDS, so only one workgroup of
@@ -284,9 +286,13 @@ static hipError_t go_linked(Ptrs<const u32x4*> s, Ptrs<u32x4*> o, uint64_t* ws, 
     const void* kernel = linked_kernel<N, U, kStream, kNtCopies, false>();
     hipError_t e;
     if constexpr (kCanStage) {
-        e = cached_capacity<linked_kernel<N, U, kStream, kNtCopies, true>>(&cap);
+        const bool diagonal = bases_congruent((const void* const*)s.p, N);
+        e = diagonal ? cached_capacity<linked_kernel<N, U, kStream, kNtCopies, true, true>>(&cap)
+                     : cached_capacity<linked_kernel<N, U, kStream, kNtCopies, true, false>>(&cap);
         if (e != hipSuccess) return e;
-        if (cap >= (int)kLinkGroups) kernel = linked_kernel<N, U, kStream, kNtCopies, true>();
+        if (cap >= (int)kLinkGroups)
+            kernel = diagonal ? linked_kernel<N, U, kStream, kNtCopies, true, true>()
+                              : linked_kernel<N, U, kStream, kNtCopies, true, false>();
     }
     if (cap < (int)kLinkGroups) {
         e = cached_capacity<linked_kernel<N, U, kStream, kNtCopies, false>>(&cap);
