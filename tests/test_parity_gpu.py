@@ -600,8 +600,8 @@ def test_staged_reduce_rank_layouts(B, D, orc, n, shape, layout):
     buffer's base agrees with rank 0's modulo 32 KiB, and the plain pipeline
     otherwise.  The rank buffers are carved from one allocation at a stride
     that is a multiple of 32 KiB (congruent) or 4 KiB more (skewed), with
-    whole 1,024-chunk tiles or a ragged tail, for the oneshot (permuted order)
-    and twoshot phase 1."""
+    whole 1,024-chunk tiles or a ragged tail, for the oneshot (permuted order),
+    twoshot phase 1 and the flag-linked twoshot's staged phase 1."""
     if shape == "whole":
         chunks = n * 1024 * -(-3840 // n)              # whole tiles, also per twoshot slice
     else:
@@ -626,7 +626,14 @@ def test_staged_reduce_rank_layouts(B, D, orc, n, shape, layout):
     B.pc_twoshot(views, outs, k)
     for o in outs:
         assert np.array_equal(D.down(o, np.uint16), want)
-    del base, views, outs
+    ws = linked_workspace(B, n, k)                      # the linked twoshot's staged phase 1
+    for o in outs:
+        o.fill_(-1)
+    B.pc_twoshot_linked(views, outs, k, ws)
+    for o in outs:
+        assert np.array_equal(D.down(o, np.uint16), want)
+    check_linked_workspace(B, D, ws, 1)
+    del base, views, outs, ws
     torch.cuda.empty_cache()
 
 
