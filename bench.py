@@ -196,6 +196,8 @@ def run_headline(d, B, synth, args, out):
       * rotated: `--steps` back-to-back calls cycling three distinct input
         sets of 8 x 64 MiB, so no call finds its inputs in the 256 MiB
         last-level cache (the previous two calls moved 1.1 GiB through it);
+        a second rotation also cycles six outputs (384 MiB), so that no call
+        overwrites output lines the cache still holds from an earlier call;
       * per launch: 1,100 calls, each between its own pair of events; the
         median is the kernel-time statistic (plus the event overhead).
     Every output of every input set is checked bit for bit against the
@@ -223,6 +225,20 @@ def run_headline(d, B, synth, args, out):
         turn[0] += 1
         B.pc_reduce(sets[j], res[j], case.k)
     ms_rot = d.events_ms(rotated, 3 * max(1, args.steps // 3), 3)
+    res_more = [torch.full((case.k,), -1, dtype=torch.int16, device=d.dev) for _ in range(3)]
+    outs6 = res + res_more
+
+    def rotated_io():
+        m = turn[0] % 6
+        turn[0] += 1
+        B.pc_reduce(sets[m % 3], outs6[m], case.k)
+    turn[0] = 0
+    ms_rot_io = d.events_ms(rotated_io, 6 * max(1, args.steps // 6), 6)
+    torch.cuda.synchronize()
+    for m in range(3):
+        if not torch.equal(res_more[m], res[m]):
+            raise SystemExit(f"headline: output {m + 3} of the six-output rotation differs from output {m}")
+    del res_more, outs6
     med_us, p10_us, p90_us, count = d.per_launch_us(fn, 1100)
     g_us = d.graph_us(fn, calls=16, replays=4)
     ach = gbs(nbytes, ms * 1000.0)
@@ -231,6 +247,10 @@ def run_headline(d, B, synth, args, out):
                        "rotated_inputs": {"sets": 3, "event_us_per_launch": round(ms_rot * 1e3, 3),
                                           "gbs": round(gbs(nbytes, ms_rot * 1e3), 1),
                                           "frac_of_hbm_peak": round(gbs(nbytes, ms_rot * 1e3) / HBM_PEAK_GBS, 4)},
+                       "rotated_inputs_and_outputs": {
+                           "sets": 3, "outputs": 6, "event_us_per_launch": round(ms_rot_io * 1e3, 3),
+                           "gbs": round(gbs(nbytes, ms_rot_io * 1e3), 1),
+                           "frac_of_hbm_peak": round(gbs(nbytes, ms_rot_io * 1e3) / HBM_PEAK_GBS, 4)},
                        "per_launch_events": {"launches": count, "median_us": round(med_us, 3),
                                              "p10_us": round(p10_us, 3), "p90_us": round(p90_us, 3),
                                              "gbs_at_median": round(gbs(nbytes, med_us), 1)},
