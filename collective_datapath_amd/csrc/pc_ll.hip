@@ -49,27 +49,29 @@ __global__ __launch_bounds__(W * kWave) void k_pack_ll(const u32x4* src, u32x4* 
 // lines they make as one 16-byte store, so a wave reads 512 B and writes
 // 1 KiB, both contiguous.  (The kernel above writes two 16-byte chunks per
 // lane, so each of its store instructions covers every other chunk of the
-// output.)  At one rank: 8.6 vs 9.8 us at 16 MiB, 29.6 vs 30.7 at 64 MiB and
-// 137 vs 152 at 256 MiB; at 128 KiB the kernel above is 0.03 us faster.
-template <int W, int U>
-__global__ __launch_bounds__(W * kWave) void k_pack_ll_half(const u32x2* src, u32x4* dst, uint32_t seq,
+// output.)  A workgroup of 256 lanes takes one 2 KiB piece of the input and
+// ends, as the Atom copy's workgroups do, with device-scope stores; above
+// 64 MiB per rank its loads are non-temporal.  At one rank, against the
+// same lane mapping with two pieces per lane and default policies: 5.9 vs
+// 8.3 us at 16 MiB, 28.9 vs 29.3 at 64 MiB (33.9 vs 37.1 with the buffers
+// rotated past the last-level cache), 123 vs 137 at 256 MiB and 244 vs 270
+// at 512 MiB.  The grid is capped for the largest calls (2^32 pieces would
+// not fit the launch's 32-bit work-item count), and its workgroups then
+// loop over the pieces.
+constexpr uint32_t kPackGridCap = 1u << 22;
+
+template <int kLoadPolicy>
+__global__ __launch_bounds__(4 * kWave) void k_pack_ll_half(const u32x2* src, u32x4* dst, uint32_t seq,
                                                              size_t nhalf) {
-    constexpr int kBlk = W * kWave;
-    const size_t tile0 = (size_t)blockIdx.x * (kBlk * U);
-    u32x2 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const size_t c = tile0 + u * kBlk + threadIdx.x;
-        if (c < nhalf) v[u] = src[c];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const size_t c = tile0 + u * kBlk + threadIdx.x;
-        if (c < nhalf) {
-            u32x4 a;
-            a[0] = v[u][0]; a[1] = seq; a[2] = v[u][1]; a[3] = seq;
-            dst[c] = a;
-        }
+    constexpr uint32_t kTile = 4 * kWave;
+    const uint32_t off = threadIdx.x;
+    for (size_t first = (size_t)blockIdx.x * kTile; first < nhalf; first += (size_t)gridDim.x * kTile) {
+        const size_t left = nhalf - first;
+        const uint32_t n = (uint32_t)(left < kTile ? left : kTile);
+        const u32x2 v = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(tile_rsrc(src + first, n * 8u), off * 8u, 0, kLoadPolicy));
+        const u32x4 a = {v[0], seq, v[1], seq};
+        store16_rsrc<kPolicyDeviceScope>(tile_rsrc(dst + first, n * 16u), off * 16u, a);
     }
 }
 
@@ -244,10 +246,12 @@ hipError_t launch_pack_ll(const void* src, void* dst, size_t nchunks, uint32_t s
     if (nchunks * 16 < kSmallBytes) return go_pack<4, 1>(s, d, seq, nchunks, stream);
     const u32x2* h = reinterpret_cast<const u32x2*>(src);
     size_t nhalf = nchunks * 2;
-    constexpr size_t kTile = 4 * kWave * 2;
-    dim3 grid((unsigned)((nhalf + kTile - 1) / kTile));
+    const size_t pieces = (nhalf + 4 * kWave - 1) / (4 * kWave);
+    dim3 grid((unsigned)(pieces < kPackGridCap ? pieces : kPackGridCap));
     void* args[] = {&h, &d, &seq, &nhalf};
-    return hipLaunchKernel((const void*)&k_pack_ll_half<4, 2>, grid, dim3(4 * kWave), args, 0, stream);
+    const void* k = nchunks * 16 <= ((size_t)64 << 20) ? (const void*)&k_pack_ll_half<0>
+                                                       : (const void*)&k_pack_ll_half<kPolicyNonTemporal>;
+    return hipLaunchKernel(k, grid, dim3(4 * kWave), args, 0, stream);
 }
 
 template <int N, int W, int U>

@@ -59,32 +59,26 @@ __global__ __launch_bounds__(W * kWave) void k_publish_sentinel(const u32x4* src
     }
 }
 
-// Bandwidth regime: a persistent grid of two workgroups per CU, one 16 KiB
-// tile per step (load, barrier, store), as the Atom copy's persistent kernel.
-// Publishing in place is safe: a tile is read and then written by the same
-// workgroup, and tiles do not overlap.
-__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
-void k_publish_sentinel_persistent(const u32x4* src, u32x4* dst, size_t nchunks, uint32_t ntiles) {
-    constexpr int U = 4;
-    constexpr uint32_t kTile = 4 * kWave * U;
-    const uint32_t t = threadIdx.x;
-    for (uint32_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
-        const size_t first = (size_t)g * kTile;
-        const size_t left = nchunks - first;
-        const uint32_t bytes = (uint32_t)(left < kTile ? left : kTile) * 16u;
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src + first, bytes);
-        const __amdgpu_buffer_rsrc_t rd = tile_rsrc(dst + first, bytes);
-        u32x4 v[U];
+// From 4 MiB: the Atom copy's shape.  Short-lived workgroups of 256 lanes
+// each publish one 4 KiB tile with device-scope stores; above 32 MiB the
+// loads are non-temporal.  Against the persistent grid that walked 16 KiB
+// tiles, at one rank: 1 GiB 324 vs 360 us, 512 MiB 163 vs 174, 64 MiB 17.9
+// vs 19.6 (and 20.6 vs 24.4 with the buffers rotated past the last-level
+// cache); against the 8 KiB-per-workgroup kernel above with default
+// policies, 32 MiB 7.8 vs 10.2 us and 16 MiB 4.2 vs 4.7.  Publishing in
+// place is safe: each lane reads its chunk and then writes that chunk.
+template <int kLoadPolicy>
+__global__ __launch_bounds__(4 * kWave) void k_publish_sentinel_tile(const u32x4* src, u32x4* dst,
+                                                                      size_t nchunks) {
+    constexpr uint32_t kTile = 4 * kWave;
+    const size_t first = (size_t)blockIdx.x * kTile;
+    const size_t left = nchunks - first;
+    const uint32_t bytes = (uint32_t)(left < kTile ? left : kTile) * 16u;
+    const uint32_t off = threadIdx.x * 16u;
+    u32x4 v = load16_rsrc<kLoadPolicy>(tile_rsrc(src + first, bytes), off);
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load16_rsrc<kPolicyNonTemporal>(rs, (u * 4 * kWave + t) * 16u);
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[u][e] = sanitize(v[u][e]);
-            store16_rsrc<kPolicyDeviceScope>(rd, (u * 4 * kWave + t) * 16u, v[u]);
-        }
-    }
+    for (int e = 0; e < 4; ++e) v[e] = sanitize(v[e]);
+    store16_rsrc<kPolicyDeviceScope>(tile_rsrc(dst + first, bytes), off, v);
 }
 
 // ---- consume: every wave owns U groups of 64 consecutive packs --------------------
@@ -143,6 +137,9 @@ __global__ __launch_bounds__(W * kWave) void k_consume_sentinel(Ptrs<u32x4*> slo
 // At 8 ranks x 64 MiB on one MI355X, interleaved against the previous
 // register-batched fold and 1024-pack re-arm blocks: fold 90.7 - 91.3 us
 // against 97.6 - 98.6; re-arm 79.0 - 79.5 us against 101.2 - 101.4.
+// Device-scope re-arm stores took 75.2 against 79.4 us alone, but left the
+// re-armed lines for the next cycle's publishes to write back: eight
+// publishes and a consume then took 366 against 357 us.
 constexpr uint32_t kSDrop = 0x80000000u;  // past every tile resource
 
 template <int N>
@@ -218,22 +215,13 @@ static hipError_t go_publish(const u32x4* s, u32x4* d, size_t nchunks, hipStream
 hipError_t launch_publish_sentinel(const void* src, void* dst, size_t nchunks, hipStream_t stream) {
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
-    // Bytes read plus written.  From 512 MiB, twice the last-level cache, the
-    // persistent kernel is ahead (256 MiB per call: 76 vs 92 us); below it the
-    // one-tile-per-workgroup kernel keeps its cache help (38.2 vs 39.3 us at
-    // 128 MiB).
-    if (nchunks * 32 >= ((size_t)512 << 20)) {
-        constexpr uint32_t kTile = 4 * kWave * 4;
-        uint32_t ntiles = (uint32_t)((nchunks + kTile - 1) / kTile);
-        const uint32_t slots = 2 * device_cus();
-        const uint32_t rounds = (ntiles + slots - 1) / slots;
-        const uint32_t grid = (ntiles + rounds - 1) / rounds;
-        void* args[] = {&s, &d, &nchunks, &ntiles};
-        return hipLaunchKernel((const void*)&k_publish_sentinel_persistent, dim3(grid), dim3(4 * kWave), args, 0,
-                               stream);
-    }
     if (nchunks * 16 < kSentinelSmallBytes) return go_publish<4, 1>(s, d, nchunks, stream);
-    return go_publish<4, 2>(s, d, nchunks, stream);
+    const void* k = nchunks * 16 <= ((size_t)32 << 20) ? (const void*)&k_publish_sentinel_tile<0>
+                                                       : (const void*)&k_publish_sentinel_tile<kPolicyNonTemporal>;
+    // At most 2^31 chunks, so the grid stays below 2^23.
+    dim3 grid((unsigned)((nchunks + 4 * kWave - 1) / (4 * kWave)));
+    void* args[] = {&s, &d, &nchunks};
+    return hipLaunchKernel(k, grid, dim3(4 * kWave), args, 0, stream);
 }
 
 template <int N, int W, int U>

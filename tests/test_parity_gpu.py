@@ -187,10 +187,11 @@ def test_reduce_large_offsets_sampled(B, D, orc):
 
 # ---- Atom copy -------------------------------------------------------------------
 
-# One chunk; whole tiles plus a ragged tail (small and mid shapes); the
-# bandwidth regime from a 64 MiB working set, with a ragged last batch.
-@pytest.mark.parametrize("nbytes", [16, 16 * (256 * 3 + 5), (4 << 20) + 16 * 3, (32 << 20) + 16 * 1029,
-                                    (96 << 20) + 16 * 77])
+# One chunk; whole tiles plus a ragged tail in each policy regime (below
+# 4 MiB, 4 to 32 MiB, above 32 MiB), and exactly 32 MiB, the last size that
+# keeps the default load policy.
+@pytest.mark.parametrize("nbytes", [16, 16 * (256 * 3 + 5), (4 << 20) + 16 * 3, 32 << 20,
+                                    (32 << 20) + 16 * 1029, (96 << 20) + 16 * 77])
 def test_copy_bytes_unchanged(B, D, nbytes):
     """Every byte arrives unchanged: the expected value is the source itself
     (NaN payloads, subnormals and all other patterns included)."""
@@ -272,9 +273,12 @@ def test_pack_ll_bits(B, D, orc):
     x = synth.uniform_bf16(500, 0, 0, 8 * (512 * 3 + 7))
     assert np.array_equal(D.down(gpu_pack(B, D, x, 0xDEADBEEF), np.uint64),
                           orc.pack_ll(x, 0xDEADBEEF))
-    # Past 4 MiB per rank (two chunks per lane), with a ragged tail.
-    x = synth.uniform_bf16(501, 0, 0, 8 * ((1 << 18) + 7))
-    assert np.array_equal(D.down(gpu_pack(B, D, x, 3), np.uint64), orc.pack_ll(x, 3))
+    # Past 4 MiB per rank (8 input bytes per lane, default loads) and past
+    # 64 MiB (non-temporal loads), each with a ragged last tile.
+    for seed, chunks in ((501, (1 << 18) + 7), (502, (1 << 22) + 13)):
+        x = synth.uniform_bf16(seed, 0, 0, 8 * chunks)
+        assert np.array_equal(D.down(gpu_pack(B, D, x, 3), np.uint64), orc.pack_ll(x, 3))
+    torch.cuda.empty_cache()
 
 
 def gpu_consume(B, D, lines_dev, k, seq, out_fill=0xFFFF):
@@ -748,17 +752,19 @@ def test_publish_sentinel_bits(B, D, orc):
     t = D.up(x)                                          # in place
     B.pc_publish_sentinel(t, t, x.size)
     assert np.array_equal(D.down(t, np.uint16), orc.publish_sentinel(x))
-    # Past 4 MiB per rank (two chunks per lane), with a ragged tail.
+    # Past 4 MiB per rank (one 4 KiB tile per workgroup), with a ragged tail.
     x = synth.SentinelCase("pub big", 74, 1, 8 * ((1 << 18) + 5)).payloads()[0]
     assert np.array_equal(D.down(gpu_publish(B, D, x), np.uint16), orc.publish_sentinel(x))
 
 
-@pytest.mark.parametrize("chunks,in_place", [((1 << 24) + 5, False), ((1 << 24) + 1027, True),
-                                             ((1 << 24) - 1024, False)])
+@pytest.mark.parametrize("chunks,in_place", [(1 << 21, False), ((1 << 21) + 1, True), ((1 << 24) + 5, False),
+                                             ((1 << 24) + 1027, True)])
 def test_publish_sentinel_bandwidth_regime(B, D, orc, chunks, in_place):
-    # From 512 MiB read plus written the publisher is a persistent kernel; the
-    # first two sizes are just past that (ragged last tile, one in place), the
-    # third just below.  Uniformly random bit patterns include the sentinel.
+    # From 4 MiB the publisher takes one 4 KiB tile per workgroup, with
+    # default loads up to 32 MiB (the first size is that edge) and
+    # non-temporal ones above it (the second, in place, is one chunk past it;
+    # the last two are 256 MiB with ragged last tiles, one in place).
+    # Uniformly random bit patterns include the sentinel.
     k = 8 * chunks
     say("publish bandwidth regime", k, in_place)
     x = np.random.default_rng(chunks).integers(0, 1 << 16, k, dtype=np.uint32).astype(np.uint16)
