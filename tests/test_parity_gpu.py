@@ -699,8 +699,8 @@ def test_allgather_2m_stale(B, D, orc):
 
 
 # The last two move 768 MiB or more (records read plus payloads written),
-# where the staging loads carry the non-temporal hint; the one before sits
-# just below that.
+# where the staging loads carry the non-temporal hint and a workgroup takes
+# 32 records (half a bitmap word); the one before sits just below that.
 @pytest.mark.parametrize("n,shard_bytes,frac", [(1, 8192, 0.5), (3, 8192 * 3, 0.1),
                                                  (8, 8192 * 17, 0.0), (2, 8192 * 5, 1.0),
                                                  (8, (46 << 20) + 8192 * 7, 0.1),
