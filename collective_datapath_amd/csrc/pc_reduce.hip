@@ -20,7 +20,9 @@
 // cache use a persistent grid: with four or more ranks one workgroup per CU
 // whose loads go straight to LDS stages (k_reduce_staged, pc_staged.hpp),
 // otherwise two workgroups per CU whose loads land in registers
-// (k_reduce_persistent).  Three output modes cover the oneshot reduce,
+// (k_reduce_persistent); with one rank, and with two or three from 128 MiB
+// per rank, short-lived 8 KiB workgroups instead (k_reduce_short).  Three
+// output modes cover the oneshot reduce,
 // twoshot phase 1 and the single-launch twoshot; at the largest sizes the
 // single-launch twoshot folds first and hands its tiles out afterwards, in
 // the same launch (k_twoshot_persistent).  The two-launch twoshot's second
@@ -350,6 +352,51 @@ __global__ __launch_bounds__(kBlock) void k_copyout_dest(Ptrs<u32x4*> outs, uint
     }
 }
 
+// ---- bandwidth regime with one to three ranks: short-lived workgroups --------------
+// Workgroups of 256 lanes take one 8 KiB tile per rank (two 16-byte chunks
+// per lane) and end: non-temporal loads, the fold, device-scope stores.  With
+// few input streams the writes are a large share of the traffic, and HBM
+// takes writes fastest from many short-lived workgroups (as for the Atom
+// copy and k_copyout_dest).  At 128 MiB per rank, against the persistent
+// kernel: 1 rank 37.6 vs 41.6 us, 2 ranks 55.9 vs 61.3, 3 ranks 77.9 vs
+// 81.4; at 512 MiB 168 vs 216, 264 vs 310 and 355 vs 403.  At 32-64 MiB per
+// rank two and three ranks are level or slower this way (2 ranks, 64 MiB:
+// 29.3 vs 28.4 us), one rank is faster at every size (64 MiB: 17.8 vs 18.8).
+// From four ranks the staged kernel stays ahead (8 ranks, 256 MiB: 364 vs
+// 387 us).  Grid and tiles as k_reduce; a tile-sized buffer resource clamps
+// a ragged tile.
+template <int N, Out kOut>
+__global__ __launch_bounds__(kBlock) void k_reduce_short(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
+                                                           uint32_t nslice) {
+    static_assert(kOut != Out::kAll, "the fan-out keeps the persistent kernel");
+    constexpr int U = 2;
+    constexpr uint32_t kTile = kBlock * U;
+    const uint32_t s = kOut == Out::kOne ? 0u : blockIdx.y;
+    size_t first;
+    uint32_t chunks;
+    if constexpr (kOut == Out::kOne) {
+        const uint32_t tile0 = blockIdx.x * kTile;  // below nslice < 2^32
+        const uint32_t left = nslice - tile0;
+        first = tile0;
+        chunks = left < kTile ? left : kTile;
+    } else {
+        const SliceTile st = slice_tile(s, blockIdx.x, nslice, kTile);
+        first = st.first;
+        chunks = st.chunks;
+    }
+    const uint32_t t = threadIdx.x;
+    u32x4 v[U][N];
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, chunks * 16u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u][r] = load16_rsrc<kPolicyNonTemporal>(rs, (u * kBlock + t) * 16u);
+    }
+    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dst.p[kOut == Out::kOne ? 0 : s] + first, chunks * 16u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, fold_chunk<N>(v[u]));
+}
+
 // ---- launch table ---------------------------------------------------------------
 // Shapes by payload: small payloads (latency regime) take one chunk per lane
 // so the most workgroups start at once; mid payloads take two; payloads with
@@ -439,11 +486,27 @@ static hipError_t go_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uin
     return hipLaunchKernel(k, dim3(grid), dim3(kStageBlock), args, stage_pad_bytes<N>(), stream);
 }
 
+// Bytes per rank from which two or three ranks take k_reduce_short (one
+// rank takes it throughout the bandwidth regime).
+constexpr size_t kShortMinRankBytes = (size_t)128 << 20;
+
+template <int N, Out kOut>
+static hipError_t go_reduce_short(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
+                                  uint32_t slices, hipStream_t stream) {
+    // At most 2^31 chunks per rank: below 2^22 tiles per slice.
+    dim3 grid(slice_tiles(nslice, slices, 2 * kBlock), slices);
+    void* args[] = {&src, &dst, &nslice};
+    return hipLaunchKernel((const void*)&k_reduce_short<N, kOut>, grid, dim3(kBlock), args, 0, stream);
+}
+
 template <int N, Out kOut>
 static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                    uint32_t nslice, uint32_t slices, hipStream_t stream) {
     switch (rg) {
         case Regime::kStream:
+            if constexpr (kOut != Out::kAll && N < kStageMinRanks)
+                if (N == 1 || (size_t)nslice * slices * 16 >= kShortMinRankBytes)
+                    return go_reduce_short<N, kOut>(src, dst, nslice, slices, stream);
             if constexpr (kOut == Out::kAll || N < kStageMinRanks)
                 return go_reduce_persistent<N, kOut>(src, dst, nslice, slices, stream);
             else return go_reduce_staged<N, kOut>(src, dst, nslice, slices, stream);

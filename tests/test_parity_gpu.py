@@ -550,6 +550,28 @@ def test_bandwidth_regime_every_n(B, D, orc, n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n", [2, 3])
+def test_short_lived_reduce_few_ranks(B, D, orc, n):
+    """Two and three ranks from 128 MiB per rank take short-lived 8 KiB
+    workgroups (one rank does throughout the bandwidth regime, as in the
+    test above): the oneshot with a permuted order, and twoshot phase 1 on
+    ragged slices, each with a ragged last tile."""
+    chunks = (8 << 20) + 773                          # 128 MiB + 12,368 B per rank
+    k = 8 * chunks
+    say("short-lived reduce", n, k)
+    xs = [synth.uniform_bf16(1800 + n, 0, r, k) for r in range(n)]
+    order = list(np.random.default_rng(80 + n).permutation(n))
+    assert np.array_equal(gpu_reduce(B, D, xs, order=order),
+                          orc.reduce(xs, order=order, threads=THREADS))
+    sc = -(-chunks // n) + 5
+    k2 = 8 * n * sc
+    xs2 = [synth.uniform_bf16(1810 + n, 0, r, k2) for r in range(n)]
+    want = orc.reduce(xs2, threads=THREADS)
+    for g in gpu_twoshot(B, D, xs2, "two"):
+        assert np.array_equal(g, want)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("n", [4, 5, 8])
 def test_staged_reduce_every_batch_remainder(B, D, orc, n):
     """The LDS-staged persistent reduce (four or more ranks, working set of
