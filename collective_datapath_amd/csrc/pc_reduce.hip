@@ -21,9 +21,9 @@
 // whose loads go straight to LDS stages (k_reduce_staged, pc_staged.hpp),
 // otherwise two workgroups per CU whose loads land in registers
 // (k_reduce_persistent); with one rank, and with two or three from 128 MiB
-// per rank, short-lived 8 KiB workgroups instead (k_reduce_short).  Three
-// output modes cover the oneshot reduce,
-// twoshot phase 1 and the single-launch twoshot; at the largest sizes the
+// per rank, short-lived workgroups of 8 KiB tiles instead (k_reduce).
+// Three output modes cover the oneshot reduce, twoshot phase 1 and the
+// single-launch twoshot; at the largest sizes the
 // single-launch twoshot folds first and hands its tiles out afterwards, in
 // the same launch (k_twoshot_persistent).  The two-launch twoshot's second
 // kernel copies each owner slice out (k_copyout), at 7 and 8 ranks from
@@ -41,22 +41,71 @@ constexpr int kBlock = 256;
 // (single-launch twoshot: the owner folds its block once and distributes it).
 enum class Out { kOne, kOwner, kAll };
 
-template <int N, Out kOut, bool kStream>
-__device__ __forceinline__ void put_chunk(const Ptrs<u32x4*>& dst, uint32_t s, size_t at, u32x4 v) {
-    if constexpr (kOut == Out::kAll) {
-#pragma unroll
-        for (int r = 0; r < N; ++r) store16<kStream>(dst.p[r] + at, v);
-    } else {
-        store16<kStream>(dst.p[kOut == Out::kOwner ? s : 0] + at, v);
-    }
-}
-
 // ---- slice reduce (oneshot when there is one slice) ----------------------------
 // Grid: x = tile within a slice, y = slice.  Slice s covers chunks
 // [s*nslice, (s+1)*nslice) of every input; where its folds go is set by kOut.
-template <int N, int U, bool kStream, Out kOut>
+// A lane loads its U chunks of every rank through tile-sized buffer
+// resources (a ragged tile needs no branch), folds, and stores with
+// device-scope stores.  Per call in a graph at 8 ranks, against the kernel
+// below: the oneshot 1.71 vs 1.79 us at 8 KiB per rank and 2.10 vs 2.28 at
+// 1 MiB; the single-launch twoshot 2.27 vs 2.55 us at 256 KiB and 3.32 vs
+// 4.14 at 1 MiB.  The twoshot forms take it from 128 KiB per rank; below
+// that their small ragged slices favour the kernel below (single launch at
+// 8 KiB per rank: 1.83 vs 2.00 us).  kLoadPolicy: default for cache-resident
+// payloads; non-temporal in the bandwidth regime with one to three ranks.
+template <int N, int U, int kLoadPolicy, Out kOut>
 __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
                                                      uint32_t nslice) {
+    constexpr uint32_t kTile = kBlock * U;
+    const uint32_t s = kOut == Out::kOne ? 0u : blockIdx.y;
+    size_t first;
+    uint32_t chunks;
+    if constexpr (kOut == Out::kOne) {
+        const uint32_t tile0 = blockIdx.x * kTile;  // below nslice < 2^32
+        const uint32_t left = nslice - tile0;
+        first = tile0;
+        chunks = left < kTile ? left : kTile;
+    } else {  // several slices: the 128-byte-aligned tiles of slice_tile()
+        const SliceTile st = slice_tile(s, blockIdx.x, nslice, kTile);
+        first = st.first;
+        chunks = st.chunks;
+    }
+    const uint32_t t = threadIdx.x, bytes = chunks * 16u;
+    u32x4 v[U][N];
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, bytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u][r] = load16_rsrc<kLoadPolicy>(rs, (u * kBlock + t) * 16u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const u32x4 o = fold_chunk<N>(v[u]);
+        if constexpr (kOut == Out::kAll) {
+#pragma unroll
+            for (int r = 0; r < N; ++r) store16_tile(tile_rsrc(dst.p[r] + first, bytes), (u * kBlock + t) * 16u, o);
+        } else {
+            store16_tile(tile_rsrc(dst.p[kOut == Out::kOne ? 0 : s] + first, bytes), (u * kBlock + t) * 16u, o);
+        }
+    }
+}
+
+// The twoshot forms below 128 KiB per rank: the same mapping with 64-bit
+// addresses and default-policy stores; a ragged tile takes a guarded
+// chunk-by-chunk path, so lanes past it issue nothing.
+template <int N, Out kOut>
+__device__ __forceinline__ void put_chunk(const Ptrs<u32x4*>& dst, uint32_t s, size_t at, u32x4 v) {
+    if constexpr (kOut == Out::kAll) {
+#pragma unroll
+        for (int r = 0; r < N; ++r) dst.p[r][at] = v;
+    } else {
+        dst.p[kOut == Out::kOwner ? s : 0][at] = v;
+    }
+}
+
+template <int N, int U, Out kOut>
+__global__ __launch_bounds__(kBlock) void k_reduce_small(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
+                                                           uint32_t nslice) {
     constexpr uint32_t kTile = kBlock * U;
     const uint32_t s = kOut == Out::kOne ? 0u : blockIdx.y;
     size_t first;
@@ -65,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
         const uint32_t tile0 = blockIdx.x * kTile;
         first = tile0;
         left = nslice - tile0;
-    } else {  // several slices: the 128-byte-aligned tiles of slice_tile()
+    } else {
         const SliceTile st = slice_tile(s, blockIdx.x, nslice, kTile);
         first = st.first;
         left = st.chunks;
@@ -74,16 +123,14 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
     const u32x4* in[N];
 #pragma unroll
     for (int r = 0; r < N; ++r) in[r] = src.p[r] + first;
-
     if (left >= kTile) {
         u32x4 v[U][N];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int r = 0; r < N; ++r) v[u][r] = load16<kStream>(in[r] + u * kBlock + t);
+            for (int r = 0; r < N; ++r) v[u][r] = in[r][u * kBlock + t];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            put_chunk<N, kOut, kStream>(dst, s, first + u * kBlock + t, fold_chunk<N>(v[u]));
+        for (int u = 0; u < U; ++u) put_chunk<N, kOut>(dst, s, first + u * kBlock + t, fold_chunk<N>(v[u]));
     } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -91,8 +138,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<const u32x4*> src, Ptrs<
             if (c < left) {
                 u32x4 v[N];
 #pragma unroll
-                for (int r = 0; r < N; ++r) v[r] = load16<kStream>(in[r] + c);
-                put_chunk<N, kOut, kStream>(dst, s, first + c, fold_chunk<N>(v));
+                for (int r = 0; r < N; ++r) v[r] = in[r][c];
+                put_chunk<N, kOut>(dst, s, first + c, fold_chunk<N>(v));
             }
         }
     }
@@ -353,49 +400,16 @@ __global__ __launch_bounds__(kBlock) void k_copyout_dest(Ptrs<u32x4*> outs, uint
 }
 
 // ---- bandwidth regime with one to three ranks: short-lived workgroups --------------
-// Workgroups of 256 lanes take one 8 KiB tile per rank (two 16-byte chunks
-// per lane) and end: non-temporal loads, the fold, device-scope stores.  With
-// few input streams the writes are a large share of the traffic, and HBM
-// takes writes fastest from many short-lived workgroups (as for the Atom
-// copy and k_copyout_dest).  At 128 MiB per rank, against the persistent
-// kernel: 1 rank 37.6 vs 41.6 us, 2 ranks 55.9 vs 61.3, 3 ranks 77.9 vs
-// 81.4; at 512 MiB 168 vs 216, 264 vs 310 and 355 vs 403.  At 32-64 MiB per
-// rank two and three ranks are level or slower this way (2 ranks, 64 MiB:
-// 29.3 vs 28.4 us), one rank is faster at every size (64 MiB: 17.8 vs 18.8).
-// From four ranks the staged kernel stays ahead (8 ranks, 256 MiB: 364 vs
-// 387 us).  Grid and tiles as k_reduce; a tile-sized buffer resource clamps
-// a ragged tile.
-template <int N, Out kOut>
-__global__ __launch_bounds__(kBlock) void k_reduce_short(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
-                                                           uint32_t nslice) {
-    static_assert(kOut != Out::kAll, "the fan-out keeps the persistent kernel");
-    constexpr int U = 2;
-    constexpr uint32_t kTile = kBlock * U;
-    const uint32_t s = kOut == Out::kOne ? 0u : blockIdx.y;
-    size_t first;
-    uint32_t chunks;
-    if constexpr (kOut == Out::kOne) {
-        const uint32_t tile0 = blockIdx.x * kTile;  // below nslice < 2^32
-        const uint32_t left = nslice - tile0;
-        first = tile0;
-        chunks = left < kTile ? left : kTile;
-    } else {
-        const SliceTile st = slice_tile(s, blockIdx.x, nslice, kTile);
-        first = st.first;
-        chunks = st.chunks;
-    }
-    const uint32_t t = threadIdx.x;
-    u32x4 v[U][N];
-#pragma unroll
-    for (int r = 0; r < N; ++r) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, chunks * 16u);
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u][r] = load16_rsrc<kPolicyNonTemporal>(rs, (u * kBlock + t) * 16u);
-    }
-    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dst.p[kOut == Out::kOne ? 0 : s] + first, chunks * 16u);
-#pragma unroll
-    for (int u = 0; u < U; ++u) store16_tile(ro, (u * kBlock + t) * 16u, fold_chunk<N>(v[u]));
-}
+// k_reduce with two chunks per lane (8 KiB tiles) and non-temporal loads:
+// workgroups that fold one tile and end.  With few input streams the writes
+// are a large share of the traffic, and HBM takes writes fastest from many
+// short-lived workgroups (as for the Atom copy and k_copyout_dest).  At
+// 128 MiB per rank, against the persistent kernel: 1 rank 37.6 vs 41.6 us,
+// 2 ranks 55.9 vs 61.3, 3 ranks 77.9 vs 81.4; at 512 MiB 168 vs 216, 264 vs
+// 310 and 355 vs 403.  At 32-64 MiB per rank two and three ranks are level
+// or slower this way (2 ranks, 64 MiB: 29.3 vs 28.4 us), one rank is faster
+// at every size (64 MiB: 17.8 vs 18.8).  From four ranks the staged kernel
+// stays ahead (8 ranks, 256 MiB: 364 vs 387 us).
 
 // ---- launch table ---------------------------------------------------------------
 // Shapes by payload: small payloads (latency regime) take one chunk per lane
@@ -429,14 +443,21 @@ static Regime pick_regime(size_t nchunks_per_rank, size_t working_set) {
     return Regime::kSmall;
 }
 
-template <int N, int U, bool kStream, Out kOut>
+// Bytes per rank from which the twoshot forms store with device scope
+// (k_reduce rather than k_reduce_small, and the copy-out likewise).
+constexpr size_t kScopeStoreRankBytes = (size_t)128 << 10;
+
+template <int N, int U, int kLoadPolicy, Out kOut>
 static hipError_t go_reduce(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
                             uint32_t slices, hipStream_t stream) {
+    // At most 2^31 chunks per rank: below 2^23 tiles per slice.
     constexpr uint32_t kTile = kBlock * U;
     dim3 grid(slice_tiles(nslice, slices, kTile), slices);
     void* args[] = {&src, &dst, &nslice};
-    return hipLaunchKernel((const void*)&k_reduce<N, U, kStream, kOut>, grid, dim3(kBlock), args,
-                           0, stream);
+    const bool small = kOut != Out::kOne && (size_t)nslice * slices * 16 < kScopeStoreRankBytes;
+    const void* k = small ? (const void*)&k_reduce_small<N, U, kOut>
+                          : (const void*)&k_reduce<N, U, kLoadPolicy, kOut>;
+    return hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream);
 }
 
 template <int N, Out kOut>
@@ -486,18 +507,9 @@ static hipError_t go_reduce_staged(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uin
     return hipLaunchKernel(k, dim3(grid), dim3(kStageBlock), args, stage_pad_bytes<N>(), stream);
 }
 
-// Bytes per rank from which two or three ranks take k_reduce_short (one
-// rank takes it throughout the bandwidth regime).
+// Bytes per rank from which two or three ranks take the short-lived
+// k_reduce (one rank takes it throughout the bandwidth regime).
 constexpr size_t kShortMinRankBytes = (size_t)128 << 20;
-
-template <int N, Out kOut>
-static hipError_t go_reduce_short(Ptrs<const u32x4*> src, Ptrs<u32x4*> dst, uint32_t nslice,
-                                  uint32_t slices, hipStream_t stream) {
-    // At most 2^31 chunks per rank: below 2^22 tiles per slice.
-    dim3 grid(slice_tiles(nslice, slices, 2 * kBlock), slices);
-    void* args[] = {&src, &dst, &nslice};
-    return hipLaunchKernel((const void*)&k_reduce_short<N, kOut>, grid, dim3(kBlock), args, 0, stream);
-}
 
 template <int N, Out kOut>
 static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4*> dst,
@@ -506,12 +518,12 @@ static hipError_t go_reduce_regime(Regime rg, Ptrs<const u32x4*> src, Ptrs<u32x4
         case Regime::kStream:
             if constexpr (kOut != Out::kAll && N < kStageMinRanks)
                 if (N == 1 || (size_t)nslice * slices * 16 >= kShortMinRankBytes)
-                    return go_reduce_short<N, kOut>(src, dst, nslice, slices, stream);
+                    return go_reduce<N, 2, kPolicyNonTemporal, kOut>(src, dst, nslice, slices, stream);
             if constexpr (kOut == Out::kAll || N < kStageMinRanks)
                 return go_reduce_persistent<N, kOut>(src, dst, nslice, slices, stream);
             else return go_reduce_staged<N, kOut>(src, dst, nslice, slices, stream);
-        case Regime::kMid: return go_reduce<N, 2, false, kOut>(src, dst, nslice, slices, stream);
-        default: return go_reduce<N, 1, false, kOut>(src, dst, nslice, slices, stream);
+        case Regime::kMid: return go_reduce<N, 2, 0, kOut>(src, dst, nslice, slices, stream);
+        default: return go_reduce<N, 1, 0, kOut>(src, dst, nslice, slices, stream);
     }
 }
 
@@ -562,8 +574,14 @@ static hipError_t go_copyout(Ptrs<u32x4*> outs, uint32_t nslice, uint32_t slices
         const void* k = nt ? (const void*)&k_copyout<N, 2, kPolicyNonTemporal> : (const void*)&k_copyout<N, 2, 0>;
         return hipLaunchKernel(k, grid, dim3(kBlock), args, 0, stream);
     }
+    // From 128 KiB per rank the cache-resident copy-out stores with device
+    // scope, as the slice reduce before it (two-launch twoshot, 8 ranks, per
+    // call in a graph: 3.83 vs 4.82 us at 256 KiB per rank, 5.55 vs 6.45 at
+    // 1 MiB).
     dim3 grid(slice_tiles(nslice, slices, kBlock), slices);
-    return hipLaunchKernel((const void*)&k_copyout<N, 1, 0>, grid, dim3(kBlock), args, 0, stream);
+    const bool scoped = (size_t)nslice * slices * 16 >= kScopeStoreRankBytes;
+    return hipLaunchKernel(scoped ? (const void*)&k_copyout<N, 1, kPolicyDeviceScope> : (const void*)&k_copyout<N, 1, 0>,
+                           grid, dim3(kBlock), args, 0, stream);
 }
 
 static void fill_src(Ptrs<const u32x4*>& p, const void* const* src, int n) {
