@@ -13,13 +13,13 @@
 // copies is written fastest by many workgroups that write a few KiB each and
 // end, so this beats a persistent grid that walks tiles in batches (at
 // 1 GiB: 324 vs 360 us; 512 MiB: 163 vs 173; 256 MiB: 74.6 vs 75.0 warm and
-// 82.4 vs 84.7 us with the buffers rotated past the last-level cache).  From
-// 4 MiB the stores are device-scope (32 MiB: 7.9 vs 9.7 us with the default
-// policy; 8 MiB: 2.8 vs 3.1), and above 32 MiB the loads are non-temporal
-// (64 MiB: 17.7 vs 19.4 us; 1 GiB: 324 vs 342), while up to 32 MiB the
-// source still benefits from the caches (32 MiB: 7.9 vs 9.2 us).  Below
-// 4 MiB the default policies are level with the others.  A tile-sized buffer
-// resource clamps the ragged last tile, so no lane needs a bounds branch.
+// 82.4 vs 84.7 us with the buffers rotated past the last-level cache).  The
+// stores are device-scope at every size (32 MiB: 7.9 vs 9.7 us with the
+// default policy; 8 MiB: 2.8 vs 3.1; 1 MiB in a graph: 1.57 vs 1.85), and
+// above 32 MiB the loads are non-temporal (64 MiB: 17.7 vs 19.4 us; 1 GiB:
+// 324 vs 342), while up to 32 MiB the source still benefits from the caches
+// (32 MiB: 7.9 vs 9.2 us).  A tile-sized buffer resource clamps the ragged
+// last tile, so no lane needs a bounds branch.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
 
@@ -41,9 +41,8 @@ hipError_t launch_copy(const void* src, void* dst, size_t nchunks, hipStream_t s
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
     const size_t bytes = nchunks * 16;
-    const void* k = bytes < ((size_t)4 << 20)    ? (const void*)&k_copy<0, 0>
-                    : bytes <= ((size_t)32 << 20) ? (const void*)&k_copy<0, kPolicyDeviceScope>
-                                                  : (const void*)&k_copy<kPolicyNonTemporal, kPolicyDeviceScope>;
+    const void* k = bytes <= ((size_t)32 << 20) ? (const void*)&k_copy<0, kPolicyDeviceScope>
+                                                : (const void*)&k_copy<kPolicyNonTemporal, kPolicyDeviceScope>;
     // At most 2^31 chunks (the largest copy), so the grid stays below 2^23.
     dim3 grid((unsigned)((nchunks + kCopyBlock - 1) / kCopyBlock));
     void* args[] = {&s, &d, &nchunks};

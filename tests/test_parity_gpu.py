@@ -187,9 +187,9 @@ def test_reduce_large_offsets_sampled(B, D, orc):
 
 # ---- Atom copy -------------------------------------------------------------------
 
-# One chunk; whole tiles plus a ragged tail in each policy regime (below
-# 4 MiB, 4 to 32 MiB, above 32 MiB), and exactly 32 MiB, the last size that
-# keeps the default load policy.
+# One chunk; whole tiles plus a ragged tail at several sizes on both sides
+# of 32 MiB (default loads up to it, non-temporal above), and exactly
+# 32 MiB, the last size that keeps the default load policy.
 @pytest.mark.parametrize("nbytes", [16, 16 * (256 * 3 + 5), (4 << 20) + 16 * 3, 32 << 20,
                                     (32 << 20) + 16 * 1029, (96 << 20) + 16 * 77])
 def test_copy_bytes_unchanged(B, D, nbytes):
