@@ -32,14 +32,8 @@ struct Ptrs {
 };
 
 // ---- loads and stores -------------------------------------------------------
-// Streaming (non-temporal) variants are used when the working set is far
-// larger than the caches, so one pass does not evict data that is reused.
-template <bool kStream>
-__device__ __forceinline__ u32x4 load16(const u32x4* p) {
-    if constexpr (kStream) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-
+// A 16-byte store through a 64-bit address; the streaming (non-temporal)
+// variant keeps data that is written once from evicting data that is reused.
 template <bool kStream>
 __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
     if constexpr (kStream) __builtin_nontemporal_store(v, p);
