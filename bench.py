@@ -39,18 +39,18 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain 256 MiB
 # copy); profiles/k_reduce_staged_8x64MiB_hbm_counters.md has the commands and
 # values.  Reported only while the kernel sources hash to what was profiled.
-TRAFFIC = {"bytes": 604575943,
+TRAFFIC = {"bytes": 604560037,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_staged.hpp",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "2bed4e4f973bf16b97a665952c62ca67c2c061eb05f99b00f1f27c9d944fc892"}
+           "sha256": "b5891ea1e7bd2050582f4c7dab5cb2f3f2ba1930d709735464a6f24b0d166c18"}
 HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0, true, true>"
 # rocprofv3 kernel-trace statistics of the same kernel over the 1,100
 # dispatches of the warm leg that `value` times, and over every dispatch of
 # the profiled run (profiles/k_reduce_staged_8x64MiB_trace.md), reported under
 # the same source-hash condition as TRAFFIC.
-KERNEL_TRACE = {"dispatches": 1100, "leg": "warm", "median_us": 86.608, "mean_us": 86.878,
-                "all_dispatches": 4509, "all_median_us": 88.428,
+KERNEL_TRACE = {"dispatches": 1100, "leg": "warm", "median_us": 87.849, "mean_us": 88.156,
+                "all_dispatches": 4509, "all_median_us": 89.228,
                 "profile": "profiles/k_reduce_staged_8x64MiB_trace.md"}
 METRIC = "N-way reduce effective HBM GB/s (% of peak) + µs latency at 8 KB–1 MB, 1 GPU"
 
