@@ -43,7 +43,7 @@ TRAFFIC = {"bytes": 604560037,
            "sources": ("collective_datapath_amd/csrc/pc_reduce.hip",
                        "collective_datapath_amd/csrc/pc_staged.hpp",
                        "collective_datapath_amd/csrc/pc_device.hpp"),
-           "sha256": "b5891ea1e7bd2050582f4c7dab5cb2f3f2ba1930d709735464a6f24b0d166c18"}
+           "sha256": "fd32a9183144f578c1aa34a98b2311eabbcb5a48e72479786575876a24bb0d2a"}
 HEADLINE_KERNEL = "pcdp::k_reduce_staged<8, (pcdp::Out)0, true, true>"
 # rocprofv3 kernel-trace statistics of the same kernel over the 1,100
 # dispatches of the warm leg that `value` times, and over every dispatch of

@@ -414,7 +414,8 @@ __global__ __launch_bounds__(kBlock) void k_copyout_dest(Ptrs<u32x4*> outs, uint
 // ---- launch table ---------------------------------------------------------------
 // Shapes by payload: small payloads (latency regime) take one chunk per lane
 // so the most workgroups start at once; mid payloads take two; payloads with
-// a working set of 64 MiB or more use the persistent kernel above.
+// a working set of 64 MiB or more use the bandwidth-regime kernels above
+// (staged from four ranks, short-lived or persistent below that).
 enum class Regime { kSmall, kMid, kStream };
 
 // Compute units of the current device, looked up once per device (256 if
@@ -434,9 +435,9 @@ uint32_t device_cus() {
 }
 
 // `working_set` is the bytes one call reads plus the bytes it writes.  The
-// persistent kernel takes over from 64 MiB: measured with inputs not in the
-// caches (the common case, since peers have just written them) it is ahead
-// from 8 MiB per rank at N = 8, and with warm caches within 2%.
+// bandwidth-regime kernels take over from 64 MiB: measured with inputs not in
+// the caches (the common case, since peers have just written them) they are
+// ahead from 8 MiB per rank at N = 8, and with warm caches within 2%.
 static Regime pick_regime(size_t nchunks_per_rank, size_t working_set) {
     if (working_set >= ((size_t)64 << 20)) return Regime::kStream;
     if (nchunks_per_rank >= (size_t)kBlock * 2 * 512) return Regime::kMid;
