@@ -14,10 +14,14 @@
 // Tile b (elems_per_flag elements) is validated by flag word b of every
 // rank.  Below a 320 MiB working set each tile has a workgroup of
 // elems_per_flag / 8 lanes; from there a persistent grid takes the tiles in
-// batches.  The retry loop is bounded by max_attempts so every kernel ends;
+// batches, folding on the LDS-staged pipeline when a tile is that
+// pipeline's 16 KiB per rank (8192 elements per flag, four or more ranks).  The retry loop is bounded by max_attempts so every kernel ends;
 // attempts[b] receives the attempt that validated (1-based) or 0.
 #include "pc_device.hpp"
 #include "pc_launch.hpp"
+#include "pc_staged.hpp"
+
+#include <type_traits>
 
 namespace pcdp {
 
@@ -205,6 +209,93 @@ void k_reduce_validated_persistent(Ptrs<const u32x4*> src, Ptrs<const uint32_t*>
     }
 }
 
+// Bandwidth regime with 8192 elements per flag and four or more ranks: a
+// tile is then 16 KiB per rank, the tile of the LDS-staged pipeline in
+// pc_staged.hpp, so the payload is folded by that pipeline (one workgroup
+// per CU, batches of 8, 4, 2 and 1 tiles, on the diagonal for rank buffers
+// whose bases agree modulo 32 KiB).  The first wave checks the batch's
+// flags while the stages fill; after the barrier every row of a tile that
+// passed is stored (a failing tile gets a zero-length resource) and failing
+// tiles go through the bounded retry one at a time, as above.  Lane t of
+// wave w holds chunk 256u + 64w + t of a tile in both paths.  At 64 MiB per
+// rank, against the register-batched kernel above, interleaved in a graph:
+// 8 ranks 90.1 - 90.3 vs 91.9 - 92.0 us, 4 ranks 50.9 - 51.1 vs 51.4.
+template <int N, bool kDiagonal>
+__global__ __launch_bounds__(kStageBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_reduce_validated_staged(Ptrs<const u32x4*> src, Ptrs<const uint32_t*> flags, u32x4* out,
+                               uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
+                               uint32_t ntiles) {
+    static_assert(N >= kStageMinRanks, "staged fold shape");
+    constexpr int U = 4;
+    constexpr uint32_t kTile = kStageTileChunks;
+    PC_STAGE_ARRAYS(N)
+    __shared__ uint32_t passed_lds, again_lds;
+    const uint32_t t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave, stride = gridDim.x;
+    const uint32_t expect = (uint32_t)N * flag;
+    for_each_stage_batch([&](auto tiles, uint32_t g0) {
+        constexpr int kTiles = decltype(tiles)::value;
+        // Every tile of a batch exists (the batches are cut to the tiles left).
+        if (t < kWave) {
+            bool ok = false;
+            if (t < (uint32_t)kTiles) {
+                uint32_t f[N];
+                load_flags<N, __HIP_MEMORY_SCOPE_WORKGROUP>(f, flags, g0 + t * stride);
+                ok = fold_flags<N>(f) == expect;
+            }
+            const uint64_t m = __ballot(ok);
+            if (t == 0) passed_lds = (uint32_t)m;
+        }
+        StageTile tile[kTiles];
+#pragma unroll
+        for (int j = 0; j < kTiles; ++j) tile[j] = {(size_t)(g0 + j * stride) * kTile, kTile * 16u};
+        std::conditional_t<kDiagonal, DiagonalBatch<N, kTiles>, StagedBatch<N, false, kTiles>> b{
+            src, tile, {PC_STAGE_LIST}, w, lane};
+        b.run();
+        __syncthreads();
+        const uint32_t passed = __builtin_amdgcn_readfirstlane(passed_lds);
+#pragma unroll
+        for (int j = 0; j < 4 * kTiles; ++j) {
+            const StageTile tl = tile[j / 4];
+            const bool keep = (passed >> (j / 4)) & 1u;
+            store16_tile(tile_rsrc(out + tl.first, keep ? tl.bytes : 0u), stage_row_offset(j, w, lane), b.res[j]);
+        }
+        if (t < (uint32_t)kTiles && ((passed >> t) & 1u)) attempts[g0 + t * stride] = 1;
+        // The rare path: retry each failing tile, one at a time.  Every
+        // branch below is uniform for the workgroup.
+#pragma unroll 1
+        for (int j = 0; j < kTiles; ++j) {
+            if ((passed >> j) & 1u) continue;
+            const uint32_t g = g0 + j * stride;
+            const size_t first = (size_t)g * kTile;
+            uint32_t accepted = 0;
+            for (uint32_t a = 2; a <= max_attempts; ++a) {
+                __syncthreads();  // every wave has read the previous verdict
+                uint32_t f[N] = {};
+                if (t == 0) load_flags<N, __HIP_MEMORY_SCOPE_AGENT>(f, flags, g);
+                u32x4 v[U][N];
+#pragma unroll
+                for (int r = 0; r < N; ++r) {
+                    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src.p[r] + first, kTile * 16u);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[u][r] = load16_rsrc<kPolicyDeviceScope>(rs, (u * kStageBlock + t) * 16u);
+                }
+                if (t == 0) again_lds = fold_flags<N>(f) == expect;
+                __syncthreads();
+                if (__builtin_amdgcn_readfirstlane(again_lds)) {
+                    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(out + first, kTile * 16u);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) store16_tile(ro, (u * kStageBlock + t) * 16u, fold_chunk<N>(v[u]));
+                    accepted = a;
+                    break;
+                }
+            }
+            if (t == 0) attempts[g] = accepted;
+        }
+        __syncthreads();  // passed_lds is rewritten by the next batch
+    }, ntiles);
+}
+
 template <int N, int kLanes>
 static hipError_t go_validated(Ptrs<const u32x4*> s, Ptrs<const uint32_t*> f, u32x4* out,
                                uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
@@ -243,9 +334,27 @@ static hipError_t go_validated_persistent(Ptrs<const u32x4*> s, Ptrs<const uint3
 }
 
 template <int N>
+static hipError_t go_validated_staged(Ptrs<const u32x4*> s, Ptrs<const uint32_t*> f, u32x4* out,
+                                      uint32_t flag, uint32_t max_attempts, uint32_t* attempts,
+                                      size_t tiles, hipStream_t stream) {
+    // Whole rounds of one workgroup per CU, then as few workgroups as give
+    // that many rounds (at most one per tile).
+    uint32_t ntiles = (uint32_t)tiles;
+    const uint32_t cus = device_cus();
+    const uint32_t rounds = (ntiles + cus - 1) / cus;
+    const uint32_t grid = (ntiles + rounds - 1) / rounds;
+    const void* k = bases_congruent((const void* const*)s.p, N) ? (const void*)&k_reduce_validated_staged<N, true>
+                                                                : (const void*)&k_reduce_validated_staged<N, false>;
+    void* args[] = {&s, &f, &out, &flag, &max_attempts, &attempts, &ntiles};
+    return hipLaunchKernel(k, dim3(grid), dim3(kStageBlock), args, stage_pad_bytes<N>(), stream);
+}
+
+template <int N>
 static hipError_t go_validated_persistent_u(int u, Ptrs<const u32x4*> s, Ptrs<const uint32_t*> f,
                                             u32x4* out, uint32_t flag, uint32_t max_attempts,
                                             uint32_t* attempts, size_t tiles, hipStream_t stream) {
+    if constexpr (N >= kStageMinRanks)
+        if (u == 4) return go_validated_staged<N>(s, f, out, flag, max_attempts, attempts, tiles, stream);
     switch (u) {
         case 1: return go_validated_persistent<N, 1>(s, f, out, flag, max_attempts, attempts, tiles, stream);
         case 2: return go_validated_persistent<N, 2>(s, f, out, flag, max_attempts, attempts, tiles, stream);

@@ -1028,6 +1028,42 @@ def test_reduce_validated_bandwidth_regime(B, D, orc, n, t, tiles, in_place):
     assert np.array_equal(got_out, want_out)
 
 
+@pytest.mark.parametrize("n,tiles", [(4, 5883), (8, 3835)])
+@pytest.mark.parametrize("layout", ["congruent", "skewed"])
+def test_reduce_validated_staged_rank_layouts(B, D, orc, n, tiles, layout):
+    """At 8192 elements per flag with four or more ranks the bandwidth regime
+    folds on the LDS-staged pipeline, on the diagonal when every rank
+    buffer's base agrees with rank 0's modulo 32 KiB and plainly otherwise.
+    The rank buffers are carved from one allocation at a stride that is a
+    multiple of 32 KiB (congruent) or 4 KiB more (skewed).  A tenth of the
+    tiles carry a stale flag on some rank and go through the retries.  On
+    256 CUs the tile counts give most workgroups 23 (n = 4) or 15 (n = 8)
+    tiles, so batches of 8, 4, 2 and 1 tiles all run."""
+    t = 8192
+    k = t * tiles
+    assert (n + 1) * 2 * k >= 320 << 20
+    stride = -(-2 * k // 32768) * 32768 // 2 + (2048 if layout == "skewed" else 0)   # elements
+    say("validated staged layouts", n, tiles, layout)
+    base = torch.empty(stride * n, dtype=torch.int16, device="cuda:0")
+    views = [base[r * stride:r * stride + k] for r in range(n)]
+    congruent = all((v.data_ptr() - views[0].data_ptr()) % 32768 == 0 for v in views)
+    assert congruent == (layout == "congruent")
+    case = synth.ValidatedCase("vs", 97 + n, n, k, t, flag=0x7FFFFFFF, stale_frac=0.1)
+    xs, fl = case.payloads(), case.flags()
+    for v, x in zip(views, xs):
+        v.copy_(torch.from_numpy(x.view(np.int16)).to("cuda:0"))
+    want_out, want_ok = orc.reduce_validated(xs, fl, t, case.flag)
+    assert 0 < int(want_ok.sum()) < tiles
+    dev_fl = [torch.from_numpy(f.view(np.int32)).to("cuda:0") for f in fl]
+    out = D.filled(k, 0xFFFF)
+    at = torch.full((tiles,), -1, dtype=torch.int32, device="cuda:0")
+    B.pc_reduce_validated(views, dev_fl, out, k, t, case.flag, 2, at)
+    assert np.array_equal(D.down(at, np.uint32), want_ok)
+    assert np.array_equal(D.down(out, np.uint16), want_out)
+    del base, views, out
+    torch.cuda.empty_cache()
+
+
 # ---- graph capture and concurrent streams ------------------------------------------------
 
 def test_graph_replays_match_oracle(B, D, orc):
