@@ -997,14 +997,16 @@ def test_reduce_validated_in_place(B, D, orc):
 
 # Working sets of 320 MiB and more run on the persistent kernel (two
 # workgroups per CU taking batches of 16, 8 or, at 6144 elements per flag, 2
-# tiles).  Three tiles past that size leave the last batch of most workgroups
+# tiles), or at 8192 elements per flag with four or more ranks on the
+# LDS-staged one.  Three tiles past that size leave the last batch of most workgroups
 # partly empty.  The flag's multiple wraps mod 2^32, and a tenth of the tiles
 # carry a stale flag on some rank.
 @pytest.mark.parametrize("n,t,tiles,in_place", [(8, 8192, 2279, False), (8, 2048, 9106, False),
                                                 (8, 4096, 4555, False), (2, 4096, 13657, False),
                                                 (1, 8192, 10243, False), (5, 6144, 4555, False),
                                                 (3, 2048, 20483, False), (6, 4096, 5855, False),
-                                                (7, 8192, 2563, False), (4, 8192, 4099, True)])
+                                                (7, 8192, 2563, False), (4, 8192, 4099, True),
+                                                (5, 8192, 3415, False), (6, 8192, 2927, True)])
 def test_reduce_validated_bandwidth_regime(B, D, orc, n, t, tiles, in_place):
     k = t * tiles
     say("validated bandwidth regime", n, t, tiles, in_place)
